@@ -1,0 +1,7 @@
+"""fp64 CPU oracle for paged decode attention -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  It shares no code with the HIP library.
+"""
+from .pa_oracle import (attend, attend_partitioned, attend_workload, half_to_double,  # noqa: F401
+                        max_threads)
