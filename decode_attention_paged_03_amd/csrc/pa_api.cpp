@@ -1,0 +1,148 @@
+// pa_api.cpp -- the C ABI of libpa.so: argument validation, launch planning and
+// dispatch.  Everything before pa::launch() is plain host code with no HIP call, so the
+// error paths can be exercised on a machine without a GPU.
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include <new>
+
+#include "pa.h"
+#include "pa_internal.h"
+
+struct pa_handle {
+    pa::Plan plan;
+};
+
+namespace pa {
+
+static bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+static int ilog2(int x) {
+    int r = 0;
+    while ((1 << r) < x) ++r;
+    return r;
+}
+
+int build_plan(const pa_problem* in, Plan* pl) {
+    if (!in || !pl) return PA_ERR_INVALID_ARGUMENT;
+    pa_problem p = *in;
+    if (p.batch < 1 || p.query_heads < 1 || p.kv_heads < 1 || p.head_dim < 1 || p.page_size < 1 ||
+        p.max_pages_per_sequence < 1 || p.num_physical_pages < 1 || p.partition_size < 0 ||
+        p.max_context_length < 0)
+        return PA_ERR_INVALID_ARGUMENT;
+    if (p.query_heads % p.kv_heads) return PA_ERR_INVALID_ARGUMENT;
+    const uint32_t known = PA_FLAG_FORCE_SPLIT | PA_FLAG_FORCE_SINGLE;
+    if (p.flags & ~known) return PA_ERR_INVALID_ARGUMENT;
+    if ((p.flags & PA_FLAG_FORCE_SPLIT) && (p.flags & PA_FLAG_FORCE_SINGLE))
+        return PA_ERR_INVALID_ARGUMENT;
+    if (p.head_dim != 64 && p.head_dim != 128) return PA_ERR_UNSUPPORTED;
+    if (!is_pow2(p.page_size) || p.page_size < 8 || p.page_size > 256) return PA_ERR_UNSUPPORTED;
+
+    const long long table_tokens = (long long)p.max_pages_per_sequence * p.page_size;
+    if (table_tokens > INT32_MAX) return PA_ERR_UNSUPPORTED;
+    if (p.max_context_length == 0) p.max_context_length = (int32_t)table_tokens;
+    if (p.max_context_length > table_tokens) return PA_ERR_INVALID_ARGUMENT;
+
+    int partition = p.partition_size;
+    if (p.flags & PA_FLAG_FORCE_SINGLE) {
+        long long t = ((long long)p.max_context_length + p.page_size - 1) / p.page_size * p.page_size;
+        partition = (int)(t < p.page_size ? p.page_size : t);
+    } else if (partition == 0) {
+        partition = kDefaultPartition < p.page_size ? p.page_size : kDefaultPartition;
+    }
+    if (partition % p.page_size) return PA_ERR_INVALID_ARGUMENT;
+    if (partition / p.page_size > kMaxPartitionPages) return PA_ERR_UNSUPPORTED;
+    p.partition_size = partition;
+
+    Plan out{};
+    out.prob = p;
+    out.group = p.query_heads / p.kv_heads;
+    out.heads_per_wg = 1;
+    for (int hp = 8; hp >= 1; --hp)
+        if (out.group % hp == 0) { out.heads_per_wg = hp; break; }
+    out.n_chunks = out.group / out.heads_per_wg;
+    out.partition = partition;
+    long long nparts = ((long long)p.max_context_length + partition - 1) / partition;
+    out.n_part_max = (int)(nparts < 1 ? 1 : nparts);
+    out.ps_log2 = ilog2(p.page_size);
+    out.force_split = (p.flags & PA_FLAG_FORCE_SPLIT) != 0;
+    out.need_merge = out.force_split || out.n_part_max > 1;
+
+    const long long grid = (long long)p.batch * p.kv_heads * out.n_chunks * out.n_part_max;
+    const long long mgrid = (long long)p.batch * p.query_heads;
+    if (grid > INT32_MAX || mgrid > INT32_MAX) return PA_ERR_UNSUPPORTED;
+    out.decode_grid = grid;
+    out.merge_grid = mgrid;
+    if (out.need_merge) {
+        const size_t slots = (size_t)p.batch * p.query_heads * (size_t)out.n_part_max;
+        out.ws_ml_offset = slots * (size_t)p.head_dim * sizeof(float);
+        out.ws_bytes = out.ws_ml_offset + slots * 2 * sizeof(float);
+    }
+    *pl = out;
+    return PA_OK;
+}
+
+}  // namespace pa
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+extern "C" {
+
+pa_status pa_create(const pa_problem* problem, pa_handle** out) {
+    if (!out) return PA_ERR_INVALID_ARGUMENT;
+    *out = nullptr;
+    pa::Plan plan;
+    int st = pa::build_plan(problem, &plan);
+    if (st != PA_OK) return (pa_status)st;
+    pa_handle* h = new (std::nothrow) pa_handle;
+    if (!h) return PA_ERR_NO_MEMORY;
+    h->plan = plan;
+    *out = h;
+    return PA_OK;
+}
+
+pa_status pa_workspace_size(const pa_handle* handle, size_t* bytes) {
+    if (!handle || !bytes) return PA_ERR_INVALID_ARGUMENT;
+    *bytes = handle->plan.ws_bytes;
+    return PA_OK;
+}
+
+pa_status pa_decode(const pa_handle* handle, const void* query, const void* key_cache,
+                    const void* value_cache, const int32_t* block_tables,
+                    const int32_t* context_lengths, float scale, float* out, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream) {
+    if (!handle || !query || !key_cache || !value_cache || !block_tables || !context_lengths || !out)
+        return PA_ERR_INVALID_ARGUMENT;
+    if (!isfinite(scale)) return PA_ERR_INVALID_ARGUMENT;
+    const pa::Plan& pl = handle->plan;
+    if (!aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache) || !aligned16(out))
+        return PA_ERR_MISALIGNED;
+    if (pl.ws_bytes) {
+        if (!workspace || workspace_bytes < pl.ws_bytes) return PA_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return PA_ERR_MISALIGNED;
+    }
+    hipError_t err = pa::launch(pl, query, key_cache, value_cache, block_tables, context_lengths,
+                                scale, out, workspace, stream);
+    return err == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status pa_destroy(pa_handle* handle) {
+    delete handle;
+    return PA_OK;
+}
+
+const char* pa_status_string(int status) {
+    switch (status) {
+        case PA_OK: return "PA_OK";
+        case PA_ERR_INVALID_ARGUMENT: return "PA_ERR_INVALID_ARGUMENT";
+        case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
+        case PA_ERR_MISALIGNED: return "PA_ERR_MISALIGNED";
+        case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE";
+        case PA_ERR_HIP: return "PA_ERR_HIP";
+        case PA_ERR_NO_MEMORY: return "PA_ERR_NO_MEMORY";
+        default: return "PA_ERR_UNKNOWN";
+    }
+}
+
+}  // extern "C"

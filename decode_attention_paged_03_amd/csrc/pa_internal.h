@@ -1,0 +1,44 @@
+// pa_internal.h -- launch plan shared by the host API (pa_api.cpp) and the kernels
+// (pa_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "pa.h"
+
+namespace pa {
+
+// Largest number of pages one partition may span; the partition's block-table
+// slice is staged in LDS.
+constexpr int kMaxPartitionPages = 512;
+// Tokens per partition when the caller passes 0.
+constexpr int kDefaultPartition = 1024;
+
+struct Plan {
+    pa_problem prob;        // validated copy, defaults resolved
+    int group;              // query heads per KV head
+    int heads_per_wg;       // query heads one workgroup serves (divides group, <= 8)
+    int n_chunks;           // group / heads_per_wg
+    int partition;          // tokens per partition (multiple of page_size)
+    int n_part_max;         // ceil(max_context_length / partition), >= 1
+    int ps_log2;            // log2(page_size)
+    bool force_split;       // every sequence writes partition triples and is merged
+    bool need_merge;        // the merge kernel is launched
+    size_t ws_bytes;        // workspace bytes (0 when need_merge is false)
+    size_t ws_ml_offset;    // byte offset of the (max, sum) pairs inside the workspace
+    long long decode_grid;  // workgroups of the decode kernel
+    long long merge_grid;   // workgroups of the merge kernel
+};
+
+// Host-only validation + planning; returns a pa_status.
+int build_plan(const pa_problem* p, Plan* out);
+
+// Enqueue the decode (and, if planned, merge) kernels.  Pointers already validated.
+hipError_t launch(const Plan& plan, const void* q, const void* k, const void* v,
+                  const int32_t* block_tables, const int32_t* ctx, float scale, float* out,
+                  void* workspace, hipStream_t stream);
+
+}  // namespace pa

@@ -1,0 +1,124 @@
+/*
+ * pa.h -- C ABI of the MI355X (gfx950) paged-attention decode library (libpa.so).
+ *
+ * One call, pa_decode(), evaluates one decode step of attention for a batch of
+ * sequences whose keys and values live in a paged cache:
+ *
+ *   out[b][h][:] = sum_t softmax_t( scale * q[b][h] . K[t][g] ) * V[t][g][:]
+ *
+ * over the context_lengths[b] cached tokens t of sequence b, with query head h
+ * reading KV head g = h / (query_heads / kv_heads).  The definition is the one of
+ * the "Paged Attention" section of "[TIL] Optimizing paged attention"
+ * (retepy.com); the score is multiplied by `scale` as in that page's Baseline
+ * kernel, and query heads map to KV heads in contiguous groups as there.
+ *
+ * Cache layout ("Data Layout" section of the same page): key_cache and
+ * value_cache are pools of physical pages, each [page_size][kv_heads][head_dim]
+ * fp16, pages contiguous: element (page p, slot s, kv head g, dim d) is at
+ * ((p * page_size + s) * kv_heads + g) * head_dim + d.  Token t of sequence b is
+ * in slot t % page_size of physical page block_tables[b][t / page_size].
+ *
+ * Long contexts are split into partitions of partition_size tokens whose
+ * (max, sum, unnormalised output) triples are combined afterwards, as the
+ * "V4 (Context-axis parallelism)" section of the same page does with its split
+ * and merge kernels; a sequence that fits one partition is finished in a single
+ * pass without the workspace (the single-tile path of the
+ * "paged_attention_v2_pytorch.py" commit page).
+ *
+ * Ownership and threading: the caller owns every device buffer, the workspace
+ * and the stream; the library owns only the host-side handle.  pa_decode()
+ * allocates nothing, copies nothing to or from the host and does not
+ * synchronise: it enqueues one or two kernels on `stream` and returns.  Buffers
+ * must stay valid until the stream has passed the call.  A handle is immutable
+ * after pa_create() and may be used from several threads at once; concurrent
+ * calls need distinct workspaces.
+ *
+ * Errors: every function returns a pa_status.  Argument checks run on the host
+ * before any HIP call; device array contents (table entries, lengths) are
+ * preconditions the library does not check (see pa_decode).
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+    PA_OK = 0,
+    PA_ERR_INVALID_ARGUMENT = 1, /* null pointer, non-positive size, query_heads % kv_heads != 0,
+                                    partition_size not a multiple of page_size, ...            */
+    PA_ERR_UNSUPPORTED = 2,      /* a shape this build has no kernel for (head_dim, page_size,
+                                    partition too long)                                         */
+    PA_ERR_MISALIGNED = 3,       /* query / key_cache / value_cache / out / workspace not 16-byte
+                                    aligned                                                     */
+    PA_ERR_WORKSPACE = 4,        /* workspace missing or smaller than pa_workspace_size()        */
+    PA_ERR_HIP = 5,              /* the HIP runtime reported an error on launch                  */
+    PA_ERR_NO_MEMORY = 6         /* host allocation of the handle failed                         */
+} pa_status;
+
+/* Flags for pa_problem.flags */
+#define PA_FLAG_FORCE_SPLIT  0x1u /* route every sequence through partition triples + merge */
+#define PA_FLAG_FORCE_SINGLE 0x2u /* one partition per sequence (partition = max context)     */
+
+typedef struct pa_problem {
+    int32_t batch;                  /* number of sequences, >= 1                                  */
+    int32_t query_heads;            /* query heads per sequence, multiple of kv_heads             */
+    int32_t kv_heads;               /* KV heads, >= 1                                             */
+    int32_t head_dim;               /* 64 or 128                                                  */
+    int32_t page_size;              /* tokens per page: power of two, 8 .. 256                    */
+    int32_t max_pages_per_sequence; /* row stride of block_tables                                 */
+    int32_t num_physical_pages;     /* pages in each of key_cache / value_cache (informational)   */
+    int32_t partition_size;         /* tokens per partition, multiple of page_size, at most
+                                       512 pages; 0 -> the library's default                      */
+    int32_t max_context_length;     /* bound on every context_lengths[b]; sizes the grid and the
+                                       workspace; 0 -> max_pages_per_sequence * page_size          */
+    uint32_t flags;                 /* PA_FLAG_*                                                  */
+} pa_problem;
+
+typedef struct pa_handle pa_handle; /* opaque, host memory only */
+
+/* Validate *problem and create a handle holding a copy of it plus the launch plan.
+ * Host only: no HIP call.  On error *out is set to NULL. */
+pa_status pa_create(const pa_problem *problem, pa_handle **out);
+
+/* Bytes of device workspace pa_decode() needs for this problem (0 when no sequence can
+ * need more than one partition).  Host only. */
+pa_status pa_workspace_size(const pa_handle *handle, size_t *bytes);
+
+/* Enqueue one decode step on `stream`.
+ *   query           fp16 [batch][query_heads][head_dim], 16-byte aligned
+ *   key_cache       fp16 [pages][page_size][kv_heads][head_dim], 16-byte aligned
+ *   value_cache     fp16, same layout as key_cache
+ *   block_tables    int32 [batch][max_pages_per_sequence]
+ *   context_lengths int32 [batch]
+ *   scale           multiplies q . k (pass 1/sqrt(head_dim) for the usual scaling)
+ *   out             fp32 [batch][query_heads][head_dim], 16-byte aligned; every element is
+ *                   written (a sequence with context length 0 gets zeros)
+ *   workspace       device scratch of at least pa_workspace_size() bytes, 16-byte aligned
+ *                   (may be NULL when that size is 0); contents undefined afterwards
+ * Preconditions (not checked): 0 <= context_lengths[b] <= max_context_length, and
+ * 0 <= block_tables[b][i] < number of pages for i < ceil(context_lengths[b] / page_size).
+ * Table slots past that are never read.  Pointers are device pointers (or host-mapped
+ * memory the GPU can read). */
+pa_status pa_decode(const pa_handle *handle, const void *query, const void *key_cache,
+                    const void *value_cache, const int32_t *block_tables,
+                    const int32_t *context_lengths, float scale, float *out, void *workspace,
+                    size_t workspace_bytes, hipStream_t stream);
+
+/* Free the handle; NULL is accepted. */
+pa_status pa_destroy(pa_handle *handle);
+
+/* Static, NUL-terminated name of a status code. */
+const char *pa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

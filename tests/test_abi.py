@@ -1,0 +1,156 @@
+"""The C ABI on the host: the library loads, exports what include/pa.h declares, and
+rejects bad arguments before any HIP call (no GPU needed)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from decode_attention_paged_03_amd import pa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(pa.LIB_PATH):
+        from decode_attention_paged_03_amd import build
+        build.build()
+    return pa.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(pa_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_abi():
+    assert declared_functions() == sorted(pa.EXPORTED)
+
+
+def test_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", pa.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    syms = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in declared_functions():
+        assert name in syms, name
+        assert getattr(lib, name) is not None
+
+
+def good(**over):
+    d = dict(batch=2, query_heads=8, kv_heads=2, head_dim=128, page_size=16,
+             max_pages_per_sequence=8, num_physical_pages=16, partition_size=0,
+             max_context_length=0, flags=0)
+    d.update(over)
+    return pa.make_problem(**d)
+
+
+def create_status(prob):
+    h = ctypes.c_void_p()
+    st = pa.load().pa_create(ctypes.byref(prob), ctypes.byref(h))
+    if st == pa.PA_OK:
+        pa.pa_destroy(h)
+    else:
+        assert not h.value
+    return st
+
+
+@pytest.mark.parametrize("over,status", [
+    ({}, pa.PA_OK),
+    (dict(head_dim=64), pa.PA_OK),
+    (dict(batch=0), pa.PA_ERR_INVALID_ARGUMENT),
+    (dict(query_heads=6, kv_heads=4), pa.PA_ERR_INVALID_ARGUMENT),
+    (dict(kv_heads=0), pa.PA_ERR_INVALID_ARGUMENT),
+    (dict(head_dim=96), pa.PA_ERR_UNSUPPORTED),
+    (dict(head_dim=-1), pa.PA_ERR_INVALID_ARGUMENT),
+    (dict(page_size=12), pa.PA_ERR_UNSUPPORTED),
+    (dict(page_size=4), pa.PA_ERR_UNSUPPORTED),
+    (dict(page_size=512), pa.PA_ERR_UNSUPPORTED),
+    (dict(page_size=0), pa.PA_ERR_INVALID_ARGUMENT),
+    (dict(max_pages_per_sequence=0), pa.PA_ERR_INVALID_ARGUMENT),
+    (dict(num_physical_pages=0), pa.PA_ERR_INVALID_ARGUMENT),
+    (dict(partition_size=24), pa.PA_ERR_INVALID_ARGUMENT),
+    (dict(partition_size=-16), pa.PA_ERR_INVALID_ARGUMENT),
+    (dict(partition_size=16 * 513), pa.PA_ERR_UNSUPPORTED),
+    (dict(max_context_length=8 * 16 + 1), pa.PA_ERR_INVALID_ARGUMENT),
+    (dict(flags=0x100), pa.PA_ERR_INVALID_ARGUMENT),
+    (dict(flags=pa.PA_FLAG_FORCE_SPLIT | pa.PA_FLAG_FORCE_SINGLE), pa.PA_ERR_INVALID_ARGUMENT),
+    (dict(flags=pa.PA_FLAG_FORCE_SINGLE, max_pages_per_sequence=4096), pa.PA_ERR_UNSUPPORTED),
+])
+def test_create_validation(lib, over, status):
+    assert create_status(good(**over)) == status
+
+
+def test_create_null_arguments(lib):
+    h = ctypes.c_void_p()
+    assert lib.pa_create(None, ctypes.byref(h)) == pa.PA_ERR_INVALID_ARGUMENT
+    prob = good()
+    assert lib.pa_create(ctypes.byref(prob), None) == pa.PA_ERR_INVALID_ARGUMENT
+    assert lib.pa_destroy(None) == pa.PA_OK
+
+
+def ws_size(**over):
+    h = pa.pa_create(good(**over))
+    try:
+        return pa.pa_workspace_size(h)
+    finally:
+        pa.pa_destroy(h)
+
+
+def test_workspace_size():
+    # 8 pages * 16 tokens = 128 tokens fit one default partition: no workspace
+    assert ws_size() == 0
+    # partition of one page -> 8 partitions of (D + 2) floats per (sequence, query head)
+    assert ws_size(partition_size=16) == 2 * 8 * 8 * (128 + 2) * 4
+    assert ws_size(partition_size=16, max_context_length=40) == 2 * 8 * 3 * (128 + 2) * 4
+    assert ws_size(flags=pa.PA_FLAG_FORCE_SPLIT) == 2 * 8 * 1 * (128 + 2) * 4
+    assert ws_size(flags=pa.PA_FLAG_FORCE_SINGLE, max_pages_per_sequence=64) == 0
+
+
+def test_decode_rejects_before_any_hip_call(lib):
+    h = pa.pa_create(good(partition_size=16))
+    need = pa.pa_workspace_size(h)
+    A = 0x10000          # aligned fake device addresses: never dereferenced on these paths
+    try:
+        ok = dict(query=A, key_cache=A, value_cache=A, block_tables=A, context_lengths=A,
+                  scale=0.1, out=A, workspace=A, workspace_bytes=need, stream=0)
+
+        def status(**over):
+            a = dict(ok)
+            a.update(over)
+            return lib.pa_decode(h, a["query"], a["key_cache"], a["value_cache"],
+                                 a["block_tables"], a["context_lengths"], a["scale"], a["out"],
+                                 a["workspace"], a["workspace_bytes"], a["stream"])
+        for name in ("query", "key_cache", "value_cache", "block_tables", "context_lengths", "out"):
+            assert status(**{name: None}) == pa.PA_ERR_INVALID_ARGUMENT, name
+        for name in ("query", "key_cache", "value_cache", "out"):
+            assert status(**{name: A + 8}) == pa.PA_ERR_MISALIGNED, name
+        assert status(scale=float("nan")) == pa.PA_ERR_INVALID_ARGUMENT
+        assert status(scale=float("inf")) == pa.PA_ERR_INVALID_ARGUMENT
+        assert status(workspace=None) == pa.PA_ERR_WORKSPACE
+        assert status(workspace_bytes=need - 1) == pa.PA_ERR_WORKSPACE
+        assert status(workspace=A + 4) == pa.PA_ERR_MISALIGNED
+        assert lib.pa_decode(None, A, A, A, A, A, 0.1, A, A, need, None) == pa.PA_ERR_INVALID_ARGUMENT
+    finally:
+        pa.pa_destroy(h)
+
+
+def test_status_strings(lib):
+    names = ["PA_OK", "PA_ERR_INVALID_ARGUMENT", "PA_ERR_UNSUPPORTED", "PA_ERR_MISALIGNED",
+             "PA_ERR_WORKSPACE", "PA_ERR_HIP", "PA_ERR_NO_MEMORY"]
+    for i, n in enumerate(names):
+        assert pa.pa_status_string(i) == n
+    assert pa.pa_status_string(99) == "PA_ERR_UNKNOWN"
+
+
+def test_binding_does_not_route_through_the_oracle():
+    """The product package never imports the oracle and has no CPU fallback."""
+    pkg = os.path.join(ROOT, "decode_attention_paged_03_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", text, re.M), f
+                assert "pa_oracle" not in text and "libpa_oracle" not in text, f

@@ -1,0 +1,134 @@
+"""GPU parity: pa_decode (HIP, through the C ABI) against the fp64 CPU oracle.
+
+Bar: |gpu - oracle| <= 1e-3 * (1 + |oracle|) for every checked element; NaN canaries in
+unreferenced pages, past-the-end slots and a guard page in front of each cache must
+never reach the output.  Bitwise checks: repeated calls and physical-page relabelling.
+"""
+import numpy as np
+import pytest
+
+from decode_attention_paged_03_amd import pa
+from decode_attention_paged_03_amd import workloads as W
+
+import gpu_common as C
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    pa.load()
+    yield
+
+
+# ---------------------------------------------------------------- the five workloads
+
+@pytest.mark.parametrize("name", ["tiny", "small_batch", "batch64", "long100k"])
+def test_workload_full(name):
+    wl = W.make_named(name)
+    C.decode_and_check(wl)
+
+
+def test_mixed128_sampled():
+    """Mixed large decode at full size, checked on sampled rows: every query head of the
+    longest, the shortest and a spread of sequences (single-tile and split ones)."""
+    wl = W.make_named("mixed128")
+    ctx = wl.context_lengths
+    order = np.argsort(ctx, kind="stable")
+    seqs = sorted(set([int(order[0]), int(order[-1]), int(order[len(order) // 2])] +
+                      [int(s) for s in order[::16]]))
+    rows = [b * wl.query_heads + h for b in seqs for h in range(wl.query_heads)]
+    C.decode_and_check(wl, rows=rows, what=f"mixed128 ({len(seqs)} sequences sampled)")
+
+
+# ------------------------------------------------------- forced single / split routes
+
+@pytest.mark.parametrize("name", ["tiny", "small_batch"])
+@pytest.mark.parametrize("route", ["split_ps", "split_2ps", "force_split", "force_single",
+                                   "partition_512p"])
+def test_routes(name, route):
+    wl = W.make_named(name)
+    ps = wl.page_size
+    kw = dict(split_ps=dict(partition_size=ps), split_2ps=dict(partition_size=2 * ps),
+              force_split=dict(flags=pa.PA_FLAG_FORCE_SPLIT),
+              force_single=dict(flags=pa.PA_FLAG_FORCE_SINGLE),
+              partition_512p=dict(partition_size=512 * ps))[route]
+    C.decode_and_check(wl, what=f"{name}/{route}", **kw)
+
+
+# ---------------------------------------------------------------- shape sweep
+
+SHAPES = [
+    # (QH, KVH, D, ps, ctx list)
+    (4, 4, 128, 16, [1, 2, 15, 16, 17, 63, 64, 65, 300]),       # MHA
+    (8, 1, 128, 16, [5, 1000, 1025, 2049]),                     # MQA, G=8
+    (6, 2, 128, 8, [7, 8, 9, 1024, 1031]),                      # G=3, page 8
+    (10, 2, 64, 32, [33, 100, 2000]),                           # G=5, D=64
+    (14, 2, 128, 64, [64, 65, 1500]),                           # G=7, page 64
+    (32, 2, 128, 16, [700, 1]),                                 # G=16: two head chunks
+    (24, 2, 64, 128, [129, 3000]),                              # G=12, page 128
+    (12, 2, 128, 256, [256, 257, 2500]),                        # G=6, page 256
+    (8, 2, 64, 16, [0, 37, 0, 100]),                            # empty sequences
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"qh{s[0]}_kvh{s[1]}_d{s[2]}_ps{s[3]}")
+@pytest.mark.parametrize("partition", [0, 64])
+def test_shapes(shape, partition):
+    QH, KVH, D, ps, ctx = shape
+    part = 0 if partition == 0 else max(partition, ps)
+    wl = W.make_workload(name="shape", batch=len(ctx), query_heads=QH, kv_heads=KVH,
+                         head_dim=D, page_size=ps, context_lengths=ctx, pool="holes10",
+                         seed=7000 + QH * 31 + D + ps, partition_size=part)
+    C.decode_and_check(wl, what=f"shape {shape} partition {part}")
+
+
+def test_outlier_keys_small():
+    """Keys scaled x8 at 1% of positions with short partitions: many rescalings."""
+    wl = W.make_workload(name="outliers", batch=2, query_heads=24, kv_heads=4, head_dim=128,
+                         page_size=16, context_lengths=[5000, 3333], pool="holes10", seed=7100,
+                         outlier_fraction=0.01, outlier_factor=8.0, partition_size=256)
+    C.decode_and_check(wl)
+
+
+# ---------------------------------------------------------------- bitwise properties
+
+def test_repeat_bitwise_and_streams():
+    import torch
+    wl = W.make_named("small_batch")
+    dev = C.Device(wl)
+    dec = pa.decoder_for(wl, partition_size=256)
+    try:
+        a = dev.run(dec).clone()
+        for _ in range(5):
+            b = dev.run(dec)
+            assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+        s = torch.cuda.Stream()
+        out = torch.empty_like(a)
+        with torch.cuda.stream(s):
+            dec(dev.q, dev.k, dev.v, dev.bt, dev.ctx, wl.scale, out=out, stream=s)
+        s.synchronize()
+        assert torch.equal(a.view(torch.int32), out.view(torch.int32))
+    finally:
+        dec.close()
+
+
+def test_page_relabel_bitwise():
+    """Moving every page to another physical index (and rewriting the table) changes no
+    output bit: the kernel addresses K/V only through the block table."""
+    import torch
+    from oracle_pins import relabel_pages
+    wl = W.make_named("small_batch")
+    k, v, bt = relabel_pages(wl, 77)
+    wl2 = W.Workload(**{**wl.__dict__, "key_cache": k, "value_cache": v, "block_tables": bt})
+    outs = []
+    for w in (wl, wl2):
+        dec = pa.decoder_for(w, partition_size=512)
+        try:
+            outs.append(C.Device(w).run(dec).clone())
+        finally:
+            dec.close()
+    assert torch.equal(outs[0].view(torch.int32), outs[1].view(torch.int32))
