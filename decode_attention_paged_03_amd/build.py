@@ -20,39 +20,45 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 arithmetic.
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
-          "-Wall", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+          "-Wall", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          # no operand canonicalisation around fmaxf; NaN inputs still propagate through
+          # the arithmetic (that is hardware behaviour), the kernels test for none
+          "-fno-honor-nans"]
 
 
-def build(verbose: bool = False, asm_dir: str | None = None) -> str:
+def build(verbose: bool = False, asm_dir: str | None = None, defines=(), out: str = LIB,
+          build_dir: str | None = None) -> str:
+    """Compile the library; ``defines`` (e.g. ["PA_WAVES=8"]) override compile-time tunables."""
     objs = []
-    build_dir = os.path.join(PKG, "_build")
+    build_dir = build_dir or os.path.join(PKG, "_build")
+    extra = [f"-D{d}" for d in defines]
     os.makedirs(build_dir, exist_ok=True)
     for src in SOURCES:
         obj = os.path.join(build_dir, os.path.basename(src) + ".o")
-        cmd = [HIPCC, *COMMON, "-c", src, "-o", obj]
+        cmd = [HIPCC, *COMMON, *extra, "-c", src, "-o", obj]
         if src.endswith(".cpp"):
             cmd[1:1] = ["-x", "hip"]
         if verbose:
             print(" ".join(cmd), flush=True)
         subprocess.run(cmd, check=True)
         objs.append(obj)
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if asm_dir:
         os.makedirs(asm_dir, exist_ok=True)
         src = SOURCES[0]
-        cmd = [HIPCC, *COMMON, "--cuda-device-only", "-S", src, "-o",
+        cmd = [HIPCC, *COMMON, *extra, "--cuda-device-only", "-S", src, "-o",
                os.path.join(asm_dir, "pa_kernels.s"), "-Rpass-analysis=kernel-resource-usage"]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, check=True, capture_output=True, text=True)
         with open(os.path.join(asm_dir, "resource_usage.txt"), "w") as f:
             f.write(r.stderr)
-    return LIB
+    return out
 
 
 if __name__ == "__main__":

@@ -44,6 +44,17 @@ int build_plan(const pa_problem* in, Plan* pl) {
     if (p.max_context_length == 0) p.max_context_length = (int32_t)table_tokens;
     if (p.max_context_length > table_tokens) return PA_ERR_INVALID_ARGUMENT;
 
+    Plan out{};
+    out.group = p.query_heads / p.kv_heads;
+    out.heads_per_wg = 1;
+    for (int hp = 8; hp >= 1; --hp)
+        if (out.group % hp == 0) { out.heads_per_wg = hp; break; }
+    out.n_chunks = out.group / out.heads_per_wg;
+    out.ps_log2 = ilog2(p.page_size);
+    // No partition size and no flag: the library splits the work itself (balanced
+    // route).  A partition size or a flag asks for fixed partitions.
+    out.balanced = p.partition_size == 0 && p.flags == 0 && p.batch <= kMaxBalancedBatch;
+
     int partition = p.partition_size;
     if (p.flags & PA_FLAG_FORCE_SINGLE) {
         long long t = ((long long)p.max_context_length + p.page_size - 1) / p.page_size * p.page_size;
@@ -52,32 +63,34 @@ int build_plan(const pa_problem* in, Plan* pl) {
         partition = kDefaultPartition < p.page_size ? p.page_size : kDefaultPartition;
     }
     if (partition % p.page_size) return PA_ERR_INVALID_ARGUMENT;
-    if (partition / p.page_size > kMaxPartitionPages) return PA_ERR_UNSUPPORTED;
-    p.partition_size = partition;
-
-    Plan out{};
+    if (!out.balanced && partition / p.page_size > kMaxPartitionPages) return PA_ERR_UNSUPPORTED;
+    p.partition_size = out.balanced ? 0 : partition;
     out.prob = p;
-    out.group = p.query_heads / p.kv_heads;
-    out.heads_per_wg = 1;
-    for (int hp = 8; hp >= 1; --hp)
-        if (out.group % hp == 0) { out.heads_per_wg = hp; break; }
-    out.n_chunks = out.group / out.heads_per_wg;
     out.partition = partition;
     long long nparts = ((long long)p.max_context_length + partition - 1) / partition;
     out.n_part_max = (int)(nparts < 1 ? 1 : nparts);
-    out.ps_log2 = ilog2(p.page_size);
     out.force_split = (p.flags & PA_FLAG_FORCE_SPLIT) != 0;
-    out.need_merge = out.force_split || out.n_part_max > 1;
 
     const long long grid = (long long)p.batch * p.kv_heads * out.n_chunks * out.n_part_max;
     const long long mgrid = (long long)p.batch * p.query_heads;
-    if (grid > INT32_MAX || mgrid > INT32_MAX) return PA_ERR_UNSUPPORTED;
+    if (mgrid > INT32_MAX || (!out.balanced && grid > INT32_MAX)) return PA_ERR_UNSUPPORTED;
     out.decode_grid = grid;
     out.merge_grid = mgrid;
-    if (out.need_merge) {
-        const size_t slots = (size_t)p.batch * p.query_heads * (size_t)out.n_part_max;
+    if (out.balanced) {
+        // two partial (max, sum, acc) slots per workgroup, each for heads_per_wg heads
+        out.need_merge = true;
+        // plus one 16-byte merge record per workgroup
+        const size_t slots = (size_t)kMaxBalancedWG * 2 * out.heads_per_wg;
         out.ws_ml_offset = slots * (size_t)p.head_dim * sizeof(float);
-        out.ws_bytes = out.ws_ml_offset + slots * 2 * sizeof(float);
+        out.ws_desc_offset = out.ws_ml_offset + slots * 2 * sizeof(float);
+        out.ws_bytes = out.ws_desc_offset + (size_t)kMaxBalancedWG * 16;
+    } else {
+        out.need_merge = out.force_split || out.n_part_max > 1;
+        if (out.need_merge) {
+            const size_t slots = (size_t)p.batch * p.query_heads * (size_t)out.n_part_max;
+            out.ws_ml_offset = slots * (size_t)p.head_dim * sizeof(float);
+            out.ws_bytes = out.ws_ml_offset + slots * 2 * sizeof(float);
+        }
     }
     *pl = out;
     return PA_OK;

@@ -11,26 +11,35 @@
 
 namespace pa {
 
-// Largest number of pages one partition may span; the partition's block-table
+// Largest number of pages one fixed partition may span; the partition's block-table
 // slice is staged in LDS.
 constexpr int kMaxPartitionPages = 512;
-// Tokens per partition when the caller passes 0.
+// Tokens per partition when PA_FLAG_FORCE_SPLIT is given without a partition size.
 constexpr int kDefaultPartition = 1024;
+// Balanced route: at most this many sequences (their lengths and tile prefix sums are
+// held in LDS) and at most this many workgroups (sizes the workspace on the host,
+// without asking the device).
+constexpr int kMaxBalancedBatch = 2048;
+constexpr int kMaxBalancedWG = 4096;
 
 struct Plan {
     pa_problem prob;        // validated copy, defaults resolved
     int group;              // query heads per KV head
     int heads_per_wg;       // query heads one workgroup serves (divides group, <= 8)
     int n_chunks;           // group / heads_per_wg
+    bool balanced;          // route: even split of all token tiles over a resident grid
+    // fixed-partition route
     int partition;          // tokens per partition (multiple of page_size)
     int n_part_max;         // ceil(max_context_length / partition), >= 1
-    int ps_log2;            // log2(page_size)
     bool force_split;       // every sequence writes partition triples and is merged
-    bool need_merge;        // the merge kernel is launched
+    // both
+    int ps_log2;            // log2(page_size)
+    bool need_merge;        // a merge kernel is launched
     size_t ws_bytes;        // workspace bytes (0 when need_merge is false)
     size_t ws_ml_offset;    // byte offset of the (max, sum) pairs inside the workspace
-    long long decode_grid;  // workgroups of the decode kernel
-    long long merge_grid;   // workgroups of the merge kernel
+    size_t ws_desc_offset;  // balanced route: byte offset of the per-workgroup merge records
+    long long decode_grid;  // workgroups of the fixed-partition decode kernel
+    long long merge_grid;   // workgroups of the fixed-partition merge kernel
 };
 
 // Host-only validation + planning; returns a pa_status.

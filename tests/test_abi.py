@@ -100,11 +100,15 @@ def ws_size(**over):
 
 
 def test_workspace_size():
-    # 8 pages * 16 tokens = 128 tokens fit one default partition: no workspace
-    assert ws_size() == 0
-    # partition of one page -> 8 partitions of (D + 2) floats per (sequence, query head)
+    # no partition size, no flag: balanced route (group 4 -> 4 heads per workgroup)
+    # per workgroup (up to 4096): two partial slots of heads_per_wg rows + a 16-byte record
+    assert ws_size() == 4096 * 2 * 4 * (128 + 2) * 4 + 4096 * 16
+    assert ws_size(query_heads=24, kv_heads=4) == 4096 * 2 * 6 * (128 + 2) * 4 + 4096 * 16
+    # fixed partitions of one page -> 8 partitions of (D + 2) floats per (sequence, head)
     assert ws_size(partition_size=16) == 2 * 8 * 8 * (128 + 2) * 4
     assert ws_size(partition_size=16, max_context_length=40) == 2 * 8 * 3 * (128 + 2) * 4
+    # 128 tokens fit one fixed partition of 1024: no workspace unless split is forced
+    assert ws_size(partition_size=1024) == 0
     assert ws_size(flags=pa.PA_FLAG_FORCE_SPLIT) == 2 * 8 * 1 * (128 + 2) * 4
     assert ws_size(flags=pa.PA_FLAG_FORCE_SINGLE, max_pages_per_sequence=64) == 0
 

@@ -27,9 +27,13 @@ def gpu():
 # ---------------------------------------------------------------- the five workloads
 
 @pytest.mark.parametrize("name", ["tiny", "small_batch", "batch64", "long100k"])
-def test_workload_full(name):
+@pytest.mark.parametrize("route", ["balanced", "fixed1024"])
+def test_workload_full(name, route):
+    """Both routes on the workload: the library's balanced split (no partition size) and
+    fixed partitions of 1024 tokens."""
     wl = W.make_named(name)
-    C.decode_and_check(wl)
+    C.decode_and_check(wl, partition_size=0 if route == "balanced" else 1024,
+                       what=f"{name}/{route}")
 
 
 def test_mixed128_sampled():
@@ -41,7 +45,9 @@ def test_mixed128_sampled():
     seqs = sorted(set([int(order[0]), int(order[-1]), int(order[len(order) // 2])] +
                       [int(s) for s in order[::16]]))
     rows = [b * wl.query_heads + h for b in seqs for h in range(wl.query_heads)]
-    C.decode_and_check(wl, rows=rows, what=f"mixed128 ({len(seqs)} sequences sampled)")
+    for part in (0, 1024):
+        C.decode_and_check(wl, rows=rows, partition_size=part,
+                           what=f"mixed128 ({len(seqs)} sequences sampled, partition {part})")
 
 
 # ------------------------------------------------------- forced single / split routes
@@ -86,21 +92,23 @@ def test_shapes(shape, partition):
     C.decode_and_check(wl, what=f"shape {shape} partition {part}")
 
 
-def test_outlier_keys_small():
-    """Keys scaled x8 at 1% of positions with short partitions: many rescalings."""
+@pytest.mark.parametrize("partition", [0, 256])
+def test_outlier_keys_small(partition):
+    """Keys scaled x8 at 1% of positions: many moves of the reference max."""
     wl = W.make_workload(name="outliers", batch=2, query_heads=24, kv_heads=4, head_dim=128,
                          page_size=16, context_lengths=[5000, 3333], pool="holes10", seed=7100,
-                         outlier_fraction=0.01, outlier_factor=8.0, partition_size=256)
-    C.decode_and_check(wl)
+                         outlier_fraction=0.01, outlier_factor=8.0, partition_size=partition)
+    C.decode_and_check(wl, what=f"outliers partition {partition}")
 
 
 # ---------------------------------------------------------------- bitwise properties
 
-def test_repeat_bitwise_and_streams():
+@pytest.mark.parametrize("partition", [0, 256])
+def test_repeat_bitwise_and_streams(partition):
     import torch
     wl = W.make_named("small_batch")
     dev = C.Device(wl)
-    dec = pa.decoder_for(wl, partition_size=256)
+    dec = pa.decoder_for(wl, partition_size=partition)
     try:
         a = dev.run(dec).clone()
         for _ in range(5):
@@ -116,7 +124,8 @@ def test_repeat_bitwise_and_streams():
         dec.close()
 
 
-def test_page_relabel_bitwise():
+@pytest.mark.parametrize("partition", [0, 512])
+def test_page_relabel_bitwise(partition):
     """Moving every page to another physical index (and rewriting the table) changes no
     output bit: the kernel addresses K/V only through the block table."""
     import torch
@@ -126,7 +135,7 @@ def test_page_relabel_bitwise():
     wl2 = W.Workload(**{**wl.__dict__, "key_cache": k, "value_cache": v, "block_tables": bt})
     outs = []
     for w in (wl, wl2):
-        dec = pa.decoder_for(w, partition_size=512)
+        dec = pa.decoder_for(w, partition_size=partition)
         try:
             outs.append(C.Device(w).run(dec).clone())
         finally:
