@@ -7,14 +7,24 @@ A step is one pa_decode call over the whole batch of the workload (all sequences
 heads), with inputs resident in HBM.  To keep the 256 MB Infinity Cache from serving
 the K/V reads, consecutive steps rotate over several identical copies of the K/V pools
 (at least ~768 MB in total), so each step reads a copy that was evicted since its last
-use.  Prints one JSON line.
+use.  The K timed steps are enqueued back to back; one pair of HIP events on the
+library's stream brackets them, and the average call duration is that span / K.
+Prints one JSON line.
+
+HBM traffic (``roofline.traffic``) comes from rocprofv3 counter runs summarised under
+profiles/ by ``python bench.py --summarize-pmc FETCH_DIR WRITE_DIR --workload W``; it is
+reported only while the kernel sources still hash to what was profiled.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -23,18 +33,21 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published peak
+CSRC = os.path.join(ROOT, "decode_attention_paged_03_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+COPY_BYTES = 256 * 1024 * 1024  # the calibration copy: reads and writes this many bytes
 METRIC = "KV GB/s and % of HBM peak per decode step; decode tokens/s at batch 64"
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="batch64",
                     choices=["tiny", "small_batch", "batch64", "long100k", "mixed128"])
-    ap.add_argument("--partition", type=int, default=None,
-                    help="tokens per partition (default: the workload's, else the library's)")
+    ap.add_argument("--partition", type=int, default=0,
+                    help="tokens per fixed partition (default 0: the library splits the work)")
     ap.add_argument("--rotate-bytes", type=float, default=768e6,
                     help="total K/V bytes to rotate over (cold-cache timing); 0 = one copy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -42,7 +55,144 @@ def parse():
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for counter calibration)")
+    ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
+                    help="turn a rocprofv3 --kernel-trace --stats output folder of this bench into "
+                         "profiles/kernels_<workload>.txt")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc output folders (FETCH_SIZE, WRITE_SIZE) of "
+                         "`bench.py --copy-calibration` into profiles/traffic_<workload>.txt")
     return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the library's sources: counters taken on other sources do not apply."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".cpp", ".h")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def _counter_rows(folder: str, counter: str):
+    """Per-dispatch rows {Dispatch_Id, Kernel_Name, Counter_Value} of one counter from a
+    rocprofv3 output folder (csv or the default SQLite database)."""
+    rows = []
+    for p in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
+        with open(p) as f:
+            rows += [r for r in csv.DictReader(f) if r["Counter_Name"] == counter]
+    if not rows:
+        import sqlite3
+        for p in glob.glob(os.path.join(folder, "**", "*.db"), recursive=True):
+            db = sqlite3.connect(p)
+            q = ("select dispatch_id, kernel_name, value from counters_collection "
+                 "where counter_name = ?")
+            rows += [{"Dispatch_Id": d, "Kernel_Name": k, "Counter_Value": v}
+                     for d, k, v in db.execute(q, (counter,))]
+            db.close()
+    if not rows:
+        raise SystemExit(f"no {counter} values under {folder}")
+    return sorted(rows, key=lambda r: int(r["Dispatch_Id"]))
+
+
+def summarize_pmc(fetch_dir: str, write_dir: str, workload: str) -> str:
+    """KiB counters per dispatch -> bytes per pa_decode call.  The scale factor of each
+    counter is what it reads for the plain copy of COPY_BYTES (the last dispatches of
+    --copy-calibration) divided into COPY_BYTES."""
+    out = {}
+    for counter, folder in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _counter_rows(folder, counter)
+        copies = [r for r in rows if "copyBuffer" in r["Kernel_Name"] or "copy" in r["Kernel_Name"].lower()]
+        cal = float(copies[-1]["Counter_Value"]) * 1024.0
+        factor = COPY_BYTES / cal
+        pa_rows = [r for r in rows if re.search(r"\bpa_\w+", r["Kernel_Name"])]
+        per_kernel = {}
+        for r in pa_rows:
+            m = re.search(r"(pa_\w+)", r["Kernel_Name"])
+            name = m.group(1) if m else r["Kernel_Name"]
+            per_kernel.setdefault(name, []).append(float(r["Counter_Value"]) * 1024.0 * factor)
+        out[counter] = (factor, {k: sum(v) / len(v) for k, v in per_kernel.items()},
+                        {k: len(v) for k, v in per_kernel.items()})
+    fetch = sum(out["FETCH_SIZE"][1].values())
+    write = sum(out["WRITE_SIZE"][1].values())
+    lines = [f"# HBM traffic of one pa_decode call, workload {workload}",
+             f"kernel_source_sha256: {kernel_source_hash()}",
+             f"command_fetch: rocprofv3 --pmc FETCH_SIZE -d <dir> -- python bench.py --workload {workload} "
+             "--steps 10 --warmup 2 --no-cpu-baseline --copy-calibration",
+             f"command_write: rocprofv3 --pmc WRITE_SIZE -d <dir> -- python bench.py --workload {workload} "
+             "--steps 10 --warmup 2 --no-cpu-baseline --copy-calibration",
+             f"calibration: plain device copy of {COPY_BYTES} B; bytes = counter KiB * 1024 * factor",
+             f"fetch_factor: {out['FETCH_SIZE'][0]:.4f}",
+             f"write_factor: {out['WRITE_SIZE'][0]:.4f}"]
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        for k, v in out[counter][1].items():
+            lines.append(f"{counter} {k}: {v:.0f} B per dispatch (mean of {out[counter][2][k]})")
+    lines.append(f"fetch_bytes_per_call: {fetch:.0f}")
+    lines.append(f"write_bytes_per_call: {write:.0f}")
+    lines.append(f"traffic_bytes_per_call: {fetch + write:.0f}")
+    path = os.path.join(PROFILES, f"traffic_{workload}.txt")
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return path
+
+
+def summarize_trace(folder: str, workload: str, steps: int = 200) -> str:
+    """Per-kernel call count and average duration from rocprofv3's kernel statistics
+    (stats csv, else the SQLite database's top_kernels view)."""
+    stats = []
+    for p in glob.glob(os.path.join(folder, "**", "*kernel_stats.csv"), recursive=True):
+        with open(p) as f:
+            for r in csv.DictReader(f):
+                stats.append((r["Name"], int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+                              float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3))
+    if not stats:
+        import sqlite3
+        for p in glob.glob(os.path.join(folder, "**", "*.db"), recursive=True):
+            db = sqlite3.connect(p)
+            q = ("select name, count(*), avg(end - start), min(end - start), max(end - start) "
+                 "from kernels group by name order by sum(end - start) desc")
+            stats += [(n, c, a / 1e3, lo / 1e3, hi / 1e3) for n, c, a, lo, hi in db.execute(q)]
+            db.close()
+    lines = [f"# rocprofv3 kernel statistics, workload {workload}",
+             f"kernel_source_sha256: {kernel_source_hash()}",
+             f"command: rocprofv3 --kernel-trace --stats -d <dir> -o run -- python bench.py "
+             f"--workload {workload} --steps {steps} --no-cpu-baseline",
+             "(calls include the warm-up calls; durations in microseconds)",
+             f"{'kernel':<48} {'calls':>6} {'avg_us':>9} {'min_us':>9} {'max_us':>9}"]
+    per_call = 0.0
+    for n, c, a, lo, hi in stats:
+        m = re.search(r"(pa_\w+)(<[^(]*>)?", n)
+        short = (m.group(1) + (m.group(2) or "")) if m else n[:48]
+        lines.append(f"{short:<48} {c:>6} {a:>9.3f} {lo:>9.3f} {hi:>9.3f}")
+        if m:
+            per_call += a
+    lines.append(f"sum of pa_* kernel averages (one call): {per_call:.3f} us")
+    path = os.path.join(PROFILES, f"kernels_{workload}.txt")
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return path
+
+
+def traffic_per_call(workload: str):
+    """Bytes per call from profiles/traffic_<workload>.txt, or None when absent or taken
+    on other kernel sources."""
+    path = os.path.join(PROFILES, f"traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_call"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(wl, target_s: float):
@@ -68,18 +218,32 @@ def cpu_baseline(wl, target_s: float):
         n += 1
     n = max(n, 1)
     rows = list(range(n * QH))
+    # a sample smaller than the budget (the whole workload fits) is evaluated repeatedly
+    sample_tokens = int(np.asarray(wl.context_lengths[:n], dtype=np.int64).sum())
+    reps = 0
     t0 = time.perf_counter()
-    oracle.attend_workload(wl, rows=rows, nthreads=cores)
-    dt = time.perf_counter() - t0
-    kv_bytes = int(np.asarray(wl.context_lengths[:n], dtype=np.int64).sum()) * wl.kv_heads * wl.head_dim * 4
-    return {"value": round(kv_bytes / dt / 1e9, 6), "unit": "GB/s", "cores": cores,
+    while True:
+        oracle.attend_workload(wl, rows=rows, nthreads=cores)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= 0.75 * target_s or dt * (reps + 1) / reps > 2.0 * target_s:
+            break
+    kv_bytes = sample_tokens * wl.kv_heads * wl.head_dim * 4
+    return {"value": round(kv_bytes * reps / dt / 1e9, 6), "unit": "GB/s", "cores": cores,
             "kind": "oracle",
             "sample": f"first {n} of {wl.batch} sequences (all {QH} query heads, "
-                      f"{kv_bytes / 1e6:.1f} MB of K/V), {dt:.1f} s wall"}
+                      f"{kv_bytes / 1e6:.1f} MB of K/V) x {reps} evaluation(s), {dt:.1f} s wall, "
+                      f"{cores} OpenMP threads"}
 
 
 def main():
     args = parse()
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace, args.workload))
+        return
+    if args.summarize_pmc:
+        print(summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload))
+        return
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
               "run with --gpus 1", file=sys.stderr)
@@ -95,8 +259,7 @@ def main():
     pa.load()
 
     wl = W.make_named(args.workload)
-    part = args.partition if args.partition is not None else None
-    dec = pa.decoder_for(wl, partition_size=part)
+    dec = pa.decoder_for(wl, partition_size=args.partition)
     dev = "cuda"
     stream = torch.cuda.current_stream()
 
@@ -122,31 +285,35 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    start.record(stream)
     for i in range(args.steps):
-        starts[i].record(stream)
         step(i)
-        ends[i].record(stream)
+    end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    launch_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    region_ms = start.elapsed_time(end)
 
     ms_per_step = wall / args.steps * 1e3
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
-    avg_launch_ms = float(launch_ms.mean())
+    avg_launch_ms = region_ms / args.steps
     achieved = kv_bytes / (avg_launch_ms * 1e-3) / 1e9
 
     if args.copy_calibration:
-        n = 64 * 1024 * 1024
+        n = COPY_BYTES // 4
         src = torch.randn(n, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
 
+    traffic = traffic_per_call(wl.name) if args.partition == 0 else None
+    balanced = dec.problem.partition_size == 0 and dec.problem.flags == 0
+    kernel_name = ("pa_decode call: pa_decode_balanced + pa_merge_balanced" if balanced
+                   else "pa_decode call: pa_decode_kernel (+ pa_merge_kernel when split)")
     line = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -181,11 +348,10 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 5),
-            "traffic": None,
-            "kernel": "pa_decode (all kernels of one call)",
+            "traffic": traffic,
+            "kernel": kernel_name,
             "avg_launch_us": round(avg_launch_ms * 1e3, 3),
-            "p10_us": round(float(np.percentile(launch_ms, 10)) * 1e3, 3),
-            "p90_us": round(float(np.percentile(launch_ms, 90)) * 1e3, 3),
+            "timing": f"HIP events on the call's stream around {args.steps} back-to-back calls",
         },
     }
     dec.close()

@@ -53,7 +53,11 @@ int build_plan(const pa_problem* in, Plan* pl) {
     out.ps_log2 = ilog2(p.page_size);
     // No partition size and no flag: the library splits the work itself (balanced
     // route).  A partition size or a flag asks for fixed partitions.
-    out.balanced = p.partition_size == 0 && p.flags == 0 && p.batch <= kMaxBalancedBatch;
+    // Its tile indices are 32-bit: all (sequence, KV head, chunk) streams together hold
+    // fewer than 2^31 tiles of 16 tokens.
+    const long long max_tiles = (long long)p.batch * p.kv_heads * out.n_chunks * ((p.max_context_length + 15LL) / 16);
+    out.balanced = p.partition_size == 0 && p.flags == 0 && p.batch <= kMaxBalancedBatch &&
+                   max_tiles <= INT32_MAX;
 
     int partition = p.partition_size;
     if (p.flags & PA_FLAG_FORCE_SINGLE) {

@@ -66,6 +66,9 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 constexpr int kBufferFlags = 0x00020000;
 constexpr int kLoadNontemporal = 2;
 constexpr float kRescaleSlack = 8.0f;   // log2 units
+#ifndef PA_BAL_PRIO
+#define PA_BAL_PRIO 1   // balanced route: raise the issue priority of waves that fall behind
+#endif
 
 struct DecodeArgs {
     const _Float16* q;
@@ -109,6 +112,15 @@ __device__ __forceinline__ float row16_sum(float x) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Issue priority of the calling wave (0..3; s_setprio takes an immediate).  Between
+// waves of equal priority a SIMD favours the oldest.
+__device__ __forceinline__ void set_wave_priority(int p) {
+    if (p >= 3) __builtin_amdgcn_s_setprio(3);
+    else if (p == 2) __builtin_amdgcn_s_setprio(2);
+    else if (p == 1) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
+}
 
 __device__ __forceinline__ half8_t as_half8(const uint4& x) {
     return __builtin_bit_cast(half8_t, x);
@@ -156,19 +168,35 @@ struct Lane {
 
 // A operand of the score MFMA: head (col % QDUP) of the chunk starting at query row
 // `row0`, dims 32j + 8 grp .. +7; zero past HP heads; sign-flipped for a negative scale.
+// Split into the loads and the fix-up, so that a prefetch does not wait for its data.
 template <int D, int HP>
-__device__ __forceinline__ void load_q(const _Float16* q, size_t row0, uint32_t q_sign, const Lane& L,
-                                       half8_t (&qa)[Geo<D, HP>::UK]) {
+__device__ __forceinline__ void load_q_raw(const _Float16* q, size_t row0, const Lane& L,
+                                           uint4 (&qr)[Geo<D, HP>::UK]) {
     using G = Geo<D, HP>;
     const int hq = L.col % G::QDUP;
     const uint4* qp = reinterpret_cast<const uint4*>(q + (row0 + (hq < HP ? hq : 0)) * D);
 #pragma unroll
+    for (int j = 0; j < G::UK; ++j) qr[j] = qp[4 * j + L.grp];
+}
+template <int D, int HP>
+__device__ __forceinline__ void fix_q(const uint4 (&qr)[Geo<D, HP>::UK], uint32_t q_sign, const Lane& L,
+                                      half8_t (&qa)[Geo<D, HP>::UK]) {
+    using G = Geo<D, HP>;
+    const bool used = (L.col % G::QDUP) < HP;
+#pragma unroll
     for (int j = 0; j < G::UK; ++j) {
-        uint4 w = qp[4 * j + L.grp];
+        uint4 w = qr[j];
         w.x ^= q_sign; w.y ^= q_sign; w.z ^= q_sign; w.w ^= q_sign;
-        if (hq >= HP) w = uint4{0u, 0u, 0u, 0u};
+        if (!used) w = uint4{0u, 0u, 0u, 0u};
         qa[j] = as_half8(w);
     }
+}
+template <int D, int HP>
+__device__ __forceinline__ void load_q(const _Float16* q, size_t row0, uint32_t q_sign, const Lane& L,
+                                       half8_t (&qa)[Geo<D, HP>::UK]) {
+    uint4 qr[Geo<D, HP>::UK];
+    load_q_raw<D, HP>(q, row0, L, qr);
+    fix_q<D, HP>(qr, q_sign, L, qa);
 }
 
 // A raw buffer resource over `bytes` bytes at `base`.  Loads past `bytes` return zero
@@ -610,12 +638,14 @@ pa_merge_kernel(MergeArgs a) {
 }
 
 // ------------------------------------------------------------------------------------
-// Balanced route: a resident grid of workgroups splits all token tiles evenly.
+// Balanced route: one resident workgroup per CU splits all token tiles evenly.
 //
 // A stream is one (sequence b, KV head, head chunk): ceil(ctx_b / 16) tiles.  The
 // streams are laid end to end in the order (b, KV head, chunk); workgroup w takes the
-// tiles [w N / W, (w+1) N / W) of the N in total, and its waves split that range into
-// NW contiguous pieces.  A wave walks its piece tile by tile across stream boundaries.
+// tiles [w N / W, (w+1) N / W) of the N in total, and its NW waves split that range into
+// NW contiguous pieces.  A wave walks its piece tile by tile across stream boundaries,
+// with one tile (or DEPTH - 1 tiles ahead) in flight: many waves per CU, each with little
+// in flight, keep the memory system fuller than few waves with deep queues.
 // A stream that lies wholly inside one wave is finished by that wave (the single-pass
 // case); pieces of a stream that crosses waves are combined in LDS at the end of the
 // workgroup, and a stream that crosses workgroups leaves one (max, sum, acc) triple per
@@ -664,21 +694,28 @@ __device__ __forceinline__ int tile_prefix(const int32_t* ctx, int B, int* s_pre
     return total;
 }
 
-// Stream position of global tile t: sequence b (the smallest with KC * pref[b+1] > t),
-// stream index within the sequence sidx = kvh * n_chunks + chunk, tile lt in the stream.
-__device__ __forceinline__ void locate_tile(long long t, int B, int KC, const int* s_pref, int& b, int& sidx,
-                                            int& lt) {
+// Stream position of global tile t (0 <= t < N): sequence b (the smallest with
+// KC * pref[b+1] > t), stream index within the sequence sidx = kvh * n_chunks + chunk,
+// tile lt in the stream.  The host keeps N below 2^31.
+__device__ __forceinline__ void locate_tile(int t, int B, int KC, const int* s_pref, int& b, int& sidx, int& lt) {
     int lo = 0, hi = B - 1;
     while (lo < hi) {
         const int mid = (lo + hi) >> 1;
-        if ((long long)KC * s_pref[mid + 1] > t) hi = mid;
+        if (KC * s_pref[mid + 1] > t) hi = mid;
         else lo = mid + 1;
     }
     b = lo;
     const int Tb = s_pref[b + 1] - s_pref[b];
-    const long long off = t - (long long)KC * s_pref[b];
-    sidx = (int)(off / Tb);
-    lt = (int)(off - (long long)sidx * Tb);
+    const int off = t - KC * s_pref[b];
+    sidx = off / Tb;
+    lt = off - sidx * Tb;
+}
+
+// floor(x * N / W) for 0 <= x <= W.  Exact in double: x N < 2^53 is represented exactly,
+// and a quotient that is not an integer lies at least 1/W below the next integer, far
+// more than the rounding error of the (correctly rounded) division.
+__device__ __forceinline__ int split_point(int x, int N, int W) {
+    return (int)floor((double)x * (double)N / (double)W);
 }
 
 template <int D, int HP, int DEPTH, int NW, bool SPLIT>
@@ -689,6 +726,7 @@ pa_decode_balanced(DecodeArgs a) {
     constexpr int C4 = G::C4;
     constexpr int NT = NW * 64;
     constexpr int NS = 2 * NW;       // partial slots: a wave's first and last segment
+    static_assert(NS <= 64, "slot runs are found by one wave");
 
     extern __shared__ int s_dyn[];
     __shared__ int s_wsum[NW];
@@ -696,6 +734,8 @@ pa_decode_balanced(DecodeArgs a) {
     __shared__ float s_l[NS][HP];
     __shared__ float4_t s_acc[NS][HP][C4];
     __shared__ int s_meta[NS][3];    // stream id (-1: empty), first tile, end tile (global)
+    __shared__ int s_runs[NS + 1];   // first slot of each run of one stream's slots, then NS
+    __shared__ int s_nruns;
 
     const int B = a.batch;
     int* s_pref = s_dyn;             // [B + 1]
@@ -713,14 +753,14 @@ pa_decode_balanced(DecodeArgs a) {
             for (int i = tid; i < a.query_heads * D; i += NT) a.out[(size_t)b * a.query_heads * D + i] = 0.f;
 
     const int KC = a.kv_heads * a.n_chunks;
-    const long long N = (long long)KC * plane;
-    const long long NWG = gridDim.x;
-    const long long w = blockIdx.x;
-    const long long g0 = w * N / NWG;
-    const long long g1 = (w + 1) * N / NWG;
-    const long long wr0 = g0 + (g1 - g0) * wave / NW;
-    const long long wr1 = g0 + (g1 - g0) * (wave + 1) / NW;
-    const int nk = (int)(wr1 - wr0);
+    const int N = KC * plane;
+    const int NWG = gridDim.x;
+    const int w = blockIdx.x;
+    const int g0 = split_point(w, N, NWG);
+    const int g1 = split_point(w + 1, N, NWG);
+    const int wr0 = g0 + (int)((long long)(g1 - g0) * wave / NW);
+    const int wr1 = g0 + (int)((long long)(g1 - g0) * (wave + 1) / NW);
+    const int nk = wr1 - wr0;
 
     const int ps_log2 = a.ps_log2;
     const size_t tok_bytes = (size_t)a.kv_heads * D * 2;
@@ -735,7 +775,7 @@ pa_decode_balanced(DecodeArgs a) {
     // (wr0 + batch + i) (and, for pages of 8, the page of its second half).
     int btv = 0, btv2 = 0;
     auto load_pages = [&](int batch) {
-        const long long t = wr0 + batch + L.lane;
+        const int t = wr0 + batch + L.lane;
         if (t < wr1) {
             int b, sidx, lt;
             locate_tile(t, B, KC, s_pref, b, sidx, lt);
@@ -754,6 +794,7 @@ pa_decode_balanced(DecodeArgs a) {
     // A wave-uniform cursor over the tiles to load, and the description of a loaded tile.
     struct Desc {
         int b, sidx, lt, T, n_valid;
+        bool first;   // the tile opens a segment of this wave (its first, or a stream start)
     };
     // cursor: sequence cb, stream index cs, tile cl of cT tiles, sequence length cctx,
     // KV head ckvh of the stream (all wave-uniform)
@@ -783,8 +824,10 @@ pa_decode_balanced(DecodeArgs a) {
             ckvh = cs / a.n_chunks;
         }
     };
-    // load tile i of the wave (i < nk) with the cursor at it, into (kb, vb); describe it
-    auto load_tile = [&](int i, Desc& d, uint4 (&kb)[G::UK], uint4 (&vb)[G::UV]) {
+    // Load tile i of the wave (i < nk) with the cursor at it into (kb, vb); when it opens
+    // a segment, the segment's query rows come with it (into qb), so a new stream costs
+    // no extra round trip.
+    auto load_tile = [&](int i, Desc& d, uint4 (&kb)[G::UK], uint4 (&vb)[G::UV], uint4 (&qb)[G::UK]) {
         if ((i & 63) == 0 && i > 0) load_pages(i);
         const int kvh = ckvh;
         const int tok = cl * T;
@@ -793,6 +836,7 @@ pa_decode_balanced(DecodeArgs a) {
         d.lt = cl;
         d.T = cT;
         d.n_valid = min(T, cctx - tok);
+        d.first = (i == 0) || (cl == 0);
         const int phys = __builtin_amdgcn_readlane(btv, i & 63);
         const size_t base = (size_t)phys * page_bytes + (size_t)(tok & ((1 << ps_log2) - 1)) * tok_bytes;
         size_t base2 = base;
@@ -801,28 +845,29 @@ pa_decode_balanced(DecodeArgs a) {
         const char* vbase = a.v + (size_t)kvh * D * 2;
         load_kv<D, HP, SPLIT>(kbase + base, vbase + base, kbase + base2, vbase + base2, koff, voff,
                               (uint32_t)tok_bytes, d.n_valid, L, kb, vb);
+        if (d.first) {
+            const int chunk = cs - kvh * a.n_chunks;
+            load_q_raw<D, HP>(a.q, (size_t)cb * a.query_heads + kvh * a.group + chunk * HP, L, qb);
+        }
     };
 
     WaveState<D, HP> st;
     half8_t qa[G::UK];
-    int cur = -1;          // stream id of the open segment (-1: none)
     int seg_lt0 = 0;       // first stream tile of the open segment
     int seg_i0 = 0;        // first wave tile of the open segment
-    bool first_seg = true;
-    auto consume = [&](const Desc& d, const uint4 (&kb)[G::UK], const uint4 (&vb)[G::UV], int i) {
-        const int sid = d.b * KC + d.sidx;
-        const int kvh = d.sidx / a.n_chunks;
-        const int chunk = d.sidx - kvh * a.n_chunks;
-        const size_t row0 = (size_t)d.b * a.query_heads + kvh * a.group + chunk * HP;
-        if (sid != cur) {   // a new segment: the stream's query rows and a fresh state
-            cur = sid;
+    auto consume = [&](const Desc& d, const uint4 (&kb)[G::UK], const uint4 (&vb)[G::UV],
+                       const uint4 (&qb)[G::UK], int i) {
+        if (d.first) {   // a new segment: its query rows and a fresh state
+            fix_q<D, HP>(qb, a.q_sign, L, qa);
             seg_lt0 = d.lt;
             seg_i0 = i;
-            load_q<D, HP>(a.q, row0, a.q_sign, L, qa);
             st.reset();
         }
         st.tile(qa, kb, vb, d.n_valid, sl2, L);
         if (d.lt == d.T - 1 || i == nk - 1) {   // the segment ends here
+            const int kvh = d.sidx / a.n_chunks;
+            const int chunk = d.sidx - kvh * a.n_chunks;
+            const size_t row0 = (size_t)d.b * a.query_heads + kvh * a.group + chunk * HP;
             float lw[HP];
             st.reduce(lw);
             if (seg_lt0 == 0 && d.lt == d.T - 1) {
@@ -837,7 +882,9 @@ pa_decode_balanced(DecodeArgs a) {
                     }
                 }
             } else {
-                const int slot = 2 * wave + (first_seg ? 0 : 1);
+                // a piece of a stream that continues in another wave: slot 2 wave for the
+                // wave's first segment, 2 wave + 1 for its last one
+                const int slot = 2 * wave + (seg_i0 == 0 ? 0 : 1);
                 if (L.lane < G::LR) {
 #pragma unroll
                     for (int h = 0; h < HP; ++h) {
@@ -850,14 +897,12 @@ pa_decode_balanced(DecodeArgs a) {
                             s_m[slot][h] = st.mref[h];
                             s_l[slot][h] = lw[h];
                         }
-                        s_meta[slot][0] = sid;
-                        s_meta[slot][1] = (int)(wr0 + seg_i0);
-                        s_meta[slot][2] = (int)(wr0 + i + 1);
+                        s_meta[slot][0] = d.b * KC + d.sidx;
+                        s_meta[slot][1] = wr0 + seg_i0;
+                        s_meta[slot][2] = wr0 + i + 1;
                     }
                 }
             }
-            first_seg = false;
-            cur = -1;
         }
     };
 
@@ -867,22 +912,36 @@ pa_decode_balanced(DecodeArgs a) {
         // fixed route); a padding tile (i >= nk) repeats the last load and is not
         // consumed.
         uint4 kb[DEPTH][G::UK], vb[DEPTH][G::UV];
+        uint4 qb[DEPTH][G::UK];
         Desc dsc[DEPTH];
-        load_tile(0, dsc[0], kb[0], vb[0]);
 #pragma unroll
-        for (int d = 1; d < DEPTH - 1; ++d) {
-            if (d < nk) advance();
-            load_tile(min(d, nk - 1), dsc[d], kb[d], vb[d]);
+        for (int d = 0; d < DEPTH - 1; ++d) {
+            if (d > 0 && d < nk) advance();
+            load_tile(min(d, nk - 1), dsc[d], kb[d], vb[d], qb[d]);
         }
+        // The waves of a workgroup have equal work, but a SIMD serves its oldest wave
+        // first, so the youngest would finish last with the CU's other waves idle.  A
+        // wave's priority is therefore the quarter of its range it has left: a wave
+        // that has fallen behind is served first.
+        const int q1 = nk / 4, q2 = nk / 2, q3 = (3 * nk) / 4;
+        int prio = -1;
         for (int i = 0; i < nk; i += DEPTH) {
+            if (PA_BAL_PRIO) {
+                const int left = nk - i;
+                const int p = (left > q3) + (left > q2) + (left > q1);
+                if (p != prio) {
+                    set_wave_priority(p);
+                    prio = p;
+                }
+            }
 #pragma unroll
             for (int d = 0; d < DEPTH; ++d) {
                 const int nxt = (d + DEPTH - 1) % DEPTH;
                 const int inext = i + d + DEPTH - 1;
-                if (inext < nk) advance();
-                load_tile(min(inext, nk - 1), dsc[nxt], kb[nxt], vb[nxt]);
+                if (inext > 0 && inext < nk) advance();
+                load_tile(min(inext, nk - 1), dsc[nxt], kb[nxt], vb[nxt], qb[nxt]);
                 __builtin_amdgcn_sched_barrier(0);
-                if (i + d < nk) consume(dsc[d], kb[d], vb[d], i + d);
+                if (DEPTH == 1 || i + d < nk) consume(dsc[d], kb[d], vb[d], qb[d], i + d);
                 else __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // see below
             }
         }
@@ -890,19 +949,61 @@ pa_decode_balanced(DecodeArgs a) {
         // only at the very end -- so that no path reaches the loop header with loads
         // outstanding into registers the compiler may reuse; otherwise it inserts waits
         // into every iteration.)
+        if (PA_BAL_PRIO) set_wave_priority(0);
     }
     __syncthreads();
 
-    // Combine the partial slots of this workgroup, stream by stream (slots of one stream
-    // are consecutive).  A stream covered entirely is finished; otherwise it crosses a
-    // workgroup boundary and its triple goes to the workspace: slot 0 for the stream
-    // holding the workgroup's first tile, slot 1 for the one holding its last tile.
-    int first_sid = -1;
-    if (g1 > g0) {
-        int b, sidx, lt;
-        locate_tile(g0, B, KC, s_pref, b, sidx, lt);
-        first_sid = b * KC + sidx;
-    } else {
+    // Runs of slots: the non-empty slots of one stream are adjacent (slots are in tile
+    // order and a stream's tiles are contiguous).  Wave 0 finds where each run starts;
+    // meanwhile the last wave writes the workgroup's merge descriptor.
+    if (wave == 0) {
+        const int lane = L.lane;
+        const int sid = lane < NS ? s_meta[lane][0] : -1;
+        int last = sid;   // stream of the nearest non-empty slot at or below this one
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(last, off);
+            if (last < 0 && lane >= off) last = y;
+        }
+        int prev = __shfl_up(last, 1);
+        if (lane == 0) prev = -1;
+        const bool start = sid >= 0 && sid != prev;
+        const uint64_t bal = __builtin_amdgcn_ballot_w64(start);
+        const int idx = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+        const int nr = __popcll(bal);
+        if (start) s_runs[idx] = lane;
+        if (lane == 0) {
+            s_runs[nr] = NS;
+            s_nruns = nr;
+        }
+    }
+    if (wave == NW - 1 && L.lane == 0) {
+        // The stream holding the last tile, if it starts here and goes on, is merged by
+        // the merge kernel's blocks of this workgroup: {first output row, pieces, the
+        // workspace row of the first piece}.
+        int4 desc = {0, 0, 0, 0};
+        if (g1 > g0) {
+            int b, sidx, lt;
+            locate_tile(g1 - 1, B, KC, s_pref, b, sidx, lt);
+            const int Tb = s_pref[b + 1] - s_pref[b];
+            const int S = KC * s_pref[b] + sidx * Tb;
+            const int E = S + Tb;
+            if (E > g1 && S >= g0) {
+                // last workgroup the stream reaches: the largest x with split(x) <= E - 1,
+                // i.e. floor((E W - 1) / N) (exact in double, as for split_point)
+                int wl = (int)floor(((double)E * (double)NWG - 1.0) / (double)N);
+                wl = min(wl, NWG - 1);
+                const int kvh = sidx / a.n_chunks;
+                const int chunk = sidx - kvh * a.n_chunks;
+                desc.x = b * a.query_heads + kvh * a.group + chunk * HP;
+                desc.y = wl - w + 1;
+                desc.z = (w * 2 + (S == g0 ? 0 : 1)) * HP;
+            }
+        }
+        a.ws_desc[w] = desc;
+    }
+    if (g1 == g0) {
         // no tiles: an empty triple (weight 0) for a merge whose stream spans this
         // workgroup's (empty) range
         const size_t wslot = (size_t)w * 2 * HP;
@@ -916,46 +1017,51 @@ pa_decode_balanced(DecodeArgs a) {
             }
         }
     }
-    for (int s0 = 0; s0 < NS;) {
-        const int sid = s_meta[s0][0];
-        if (sid < 0) {
-            ++s0;
-            continue;
-        }
-        int s1 = s0 + 1;
-        while (s1 < NS && (s_meta[s1][0] == sid || s_meta[s1][0] < 0)) ++s1;
-        long long tb = s_meta[s0][1], te = s_meta[s0][2];
-        for (int s = s0 + 1; s < s1; ++s)
-            if (s_meta[s][0] == sid) {
-                tb = min(tb, (long long)s_meta[s][1]);
-                te = max(te, (long long)s_meta[s][2]);
-            }
-        const int b = sid / KC;
-        const int sidx = sid - b * KC;
-        const int Tb = s_pref[b + 1] - s_pref[b];
-        const long long S = (long long)KC * s_pref[b] + (long long)sidx * Tb;
-        const bool whole = tb == S && te == S + Tb;
-        const int kvh = sidx / a.n_chunks;
-        const int chunk = sidx - kvh * a.n_chunks;
-        const size_t row0 = (size_t)b * a.query_heads + kvh * a.group + chunk * HP;
-        const size_t wslot = ((size_t)w * 2 + (sid == first_sid ? 0 : 1)) * HP;
-        for (int idx = tid; idx < HP * C4; idx += NT) {
-            const int h = idx / C4;
-            const int d4 = idx - h * C4;
+    __syncthreads();
+
+    // Combine each run: HP * C4 threads per run, as many runs at once as the block holds.
+    // A stream covered entirely is finished; otherwise it crosses a workgroup boundary and
+    // its triple goes to the workspace: slot 0 for the stream holding the workgroup's
+    // first tile, slot 1 for the one holding its last tile.
+    constexpr int PER = HP * C4;
+    constexpr int RPAR = NT / PER;
+    static_assert(RPAR >= 1, "a run needs HP * D / 4 threads");
+    const int nr = s_nruns;
+    const int rsub = tid / PER;
+    if (rsub < RPAR) {
+        const int e = tid - rsub * PER;
+        const int h = e / C4;
+        const int d4 = e - h * C4;
+        for (int r = rsub; r < nr; r += RPAR) {
+            const int s0 = s_runs[r], s1 = s_runs[r + 1];
+            const int sid = s_meta[s0][0];
+            const int tb = s_meta[s0][1];
+            int te = s_meta[s0][2];
             float M = -INFINITY;
             for (int s = s0; s < s1; ++s)
-                if (s_meta[s][0] == sid) M = fmaxf(M, s_m[s][h]);
+                if (s_meta[s][0] >= 0) {
+                    M = fmaxf(M, s_m[s][h]);
+                    te = s_meta[s][2];
+                }
             float Ls = 0.f;
             float4_t o = {0.f, 0.f, 0.f, 0.f};
             for (int s = s0; s < s1; ++s)
-                if (s_meta[s][0] == sid) {
-                    const float e = fast_exp2(s_m[s][h] - M);
-                    Ls += e * s_l[s][h];
-                    o += e * s_acc[s][h][d4];
+                if (s_meta[s][0] >= 0) {
+                    const float f = fast_exp2(s_m[s][h] - M);
+                    Ls += f * s_l[s][h];
+                    o += f * s_acc[s][h][d4];
                 }
-            if (whole) {
+            const int b = sid / KC;
+            const int sidx = sid - b * KC;
+            const int Tb = s_pref[b + 1] - s_pref[b];
+            const int S = KC * s_pref[b] + sidx * Tb;
+            const int kvh = sidx / a.n_chunks;
+            const int chunk = sidx - kvh * a.n_chunks;
+            const size_t row0 = (size_t)b * a.query_heads + kvh * a.group + chunk * HP;
+            if (tb == S && te == S + Tb) {
                 reinterpret_cast<float4_t*>(a.out + (row0 + h) * D)[d4] = o / Ls;
             } else {
+                const size_t wslot = ((size_t)w * 2 + (tb == g0 ? 0 : 1)) * HP;
                 reinterpret_cast<float4_t*>(a.ws_acc + (wslot + h) * D)[d4] = o;
                 if (d4 == 0) {
                     a.ws_ml[(wslot + h) * 2] = M;
@@ -963,28 +1069,6 @@ pa_decode_balanced(DecodeArgs a) {
                 }
             }
         }
-        s0 = s1;
-    }
-    // merge descriptor: the stream holding the last tile, if it starts here and goes on
-    if (tid == 0) {
-        int4 desc = {0, 0, 0, 0};
-        if (g1 > g0) {
-            int b, sidx, lt;
-            locate_tile(g1 - 1, B, KC, s_pref, b, sidx, lt);
-            const int Tb = s_pref[b + 1] - s_pref[b];
-            const long long S = (long long)KC * s_pref[b] + (long long)sidx * Tb;
-            const long long E = S + Tb;
-            if (E > g1 && S >= g0) {
-                long long wl = w;
-                while (wl + 1 < NWG && (wl + 1) * N / NWG < E) ++wl;
-                const int kvh = sidx / a.n_chunks;
-                const int chunk = sidx - kvh * a.n_chunks;
-                desc.x = b * a.query_heads + kvh * a.group + chunk * HP;
-                desc.y = (int)(wl - w + 1);
-                desc.z = (int)(((long long)w * 2 + (S == g0 ? 0 : 1)) * HP);
-            }
-        }
-        a.ws_desc[w] = desc;
     }
 }
 
@@ -1026,25 +1110,25 @@ int resident_grid(K kernel, int block, size_t lds) {
     return (int)(g < kMaxBalancedWG ? g : kMaxBalancedWG);
 }
 
-#ifndef PA_OVERSUB
-#define PA_OVERSUB 1   // balanced grid = this many times the resident workgroups
+#ifndef PA_BAL_WAVES
+#define PA_BAL_WAVES 12  // waves per balanced workgroup (one workgroup per CU)
 #endif
 #ifndef PA_BAL_DEPTH
-#define PA_BAL_DEPTH 2   // tile buffers per wave (balanced route)
+#define PA_BAL_DEPTH 1   // tile buffers per wave (balanced route)
 #endif
-#ifndef PA_LDS_PAD
-#define PA_LDS_PAD 0     // extra LDS per balanced workgroup (limits workgroups per CU)
-#endif
+constexpr int kBalWaves = PA_BAL_WAVES;
 constexpr int kBalDepth = PA_BAL_DEPTH;
 
 template <int D, int HP, bool SPLIT>
 hipError_t launch_balanced(const Plan& pl, const DecodeArgs& args, hipStream_t stream) {
-    const auto kern = pa_decode_balanced<D, HP, kBalDepth, kWaves, SPLIT>;
-    const size_t lds = (size_t)(2 * pl.prob.batch + 1) * sizeof(int) + PA_LDS_PAD;
-    int grid = resident_grid(kern, kWaves * 64, lds) * PA_OVERSUB;
+    // 12 waves (3 per SIMD) fit the register budget up to 6 heads (4 with pages of 8);
+    // more heads take 8 waves
+    constexpr int NW = (HP <= 4 || (HP <= 6 && !SPLIT)) ? kBalWaves : 8;
+    const auto kern = pa_decode_balanced<D, HP, kBalDepth, NW, SPLIT>;
+    const size_t lds = (size_t)(2 * pl.prob.batch + 1) * sizeof(int);
+    const int grid = resident_grid(kern, NW * 64, lds);
     if (grid <= 0) return hipErrorInvalidDevice;
-    if (grid > kMaxBalancedWG) grid = kMaxBalancedWG;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kWaves * 64), lds, stream, args);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NW * 64), lds, stream, args);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL((pa_merge_balanced<D, HP>), dim3((unsigned)(grid * HP)), dim3(kMergeThreads), 0,
