@@ -18,6 +18,24 @@ namespace pa {
 
 static bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
+static int gcd(int a, int b) {
+    while (b) {
+        const int t = a % b;
+        a = b;
+        b = t;
+    }
+    return a;
+}
+
+// Waves per balanced workgroup (12: three per SIMD, which the kernels' register use
+// allows; more waves, each with one tile in flight, keep more of the memory system busy).
+static int balanced_waves(int /*streams*/) {
+#ifdef PA_BAL_WAVES
+    if (PA_BAL_WAVES == 8 || PA_BAL_WAVES == 12 || PA_BAL_WAVES == 16) return PA_BAL_WAVES;
+#endif
+    return 12;
+}
+
 static int ilog2(int x) {
     int r = 0;
     while ((1 << r) < x) ++r;
@@ -47,7 +65,7 @@ int build_plan(const pa_problem* in, Plan* pl) {
     Plan out{};
     out.group = p.query_heads / p.kv_heads;
     out.heads_per_wg = 1;
-    for (int hp = 8; hp >= 1; --hp)
+    for (int hp = kMaxHeadsPerWave; hp >= 1; --hp)
         if (out.group % hp == 0) { out.heads_per_wg = hp; break; }
     out.n_chunks = out.group / out.heads_per_wg;
     out.ps_log2 = ilog2(p.page_size);
@@ -81,12 +99,18 @@ int build_plan(const pa_problem* in, Plan* pl) {
     out.decode_grid = grid;
     out.merge_grid = mgrid;
     if (out.balanced) {
-        // two partial (max, sum, acc) slots per workgroup, each for heads_per_wg heads
+        const int streams = p.kv_heads * out.n_chunks;
+        out.bal_waves = balanced_waves(streams);
+        out.spw = gcd(streams, out.bal_waves);
+        out.waves_per_stream = out.bal_waves / out.spw;
+        out.bands = streams / out.spw;
+        // Rows of D floats (plus a (max, sum) pair each): per workgroup (up to
+        // kMaxBalancedWG), two sides x spw streams x heads_per_wg heads of piece
+        // triples; then one 16-byte merge record per workgroup.
         out.need_merge = true;
-        // plus one 16-byte merge record per workgroup
-        const size_t slots = (size_t)kMaxBalancedWG * 2 * out.heads_per_wg;
-        out.ws_ml_offset = slots * (size_t)p.head_dim * sizeof(float);
-        out.ws_desc_offset = out.ws_ml_offset + slots * 2 * sizeof(float);
+        const size_t rows = (size_t)kMaxBalancedWG * 2 * out.spw * out.heads_per_wg;
+        out.ws_ml_offset = rows * (size_t)p.head_dim * sizeof(float);
+        out.ws_desc_offset = out.ws_ml_offset + rows * 2 * sizeof(float);
         out.ws_bytes = out.ws_desc_offset + (size_t)kMaxBalancedWG * 16;
     } else {
         out.need_merge = out.force_split || out.n_part_max > 1;

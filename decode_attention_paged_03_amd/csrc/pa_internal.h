@@ -17,10 +17,13 @@ constexpr int kMaxPartitionPages = 512;
 // Tokens per partition when PA_FLAG_FORCE_SPLIT is given without a partition size.
 constexpr int kDefaultPartition = 1024;
 // Balanced route: at most this many sequences (their lengths and tile prefix sums are
-// held in LDS) and at most this many workgroups (sizes the workspace on the host,
-// without asking the device).
+// held in LDS) and at most this many workgroups, one per compute unit (sizes the
+// workspace on the host, without asking the device).
 constexpr int kMaxBalancedBatch = 2048;
-constexpr int kMaxBalancedWG = 4096;
+constexpr int kMaxBalancedWG = 1024;
+// Query heads one wave scores at once (MFMA rows are 16; LDS partial slots are sized
+// for this many heads).
+constexpr int kMaxHeadsPerWave = 8;
 
 struct Plan {
     pa_problem prob;        // validated copy, defaults resolved
@@ -28,6 +31,10 @@ struct Plan {
     int heads_per_wg;       // query heads one workgroup serves (divides group, <= 8)
     int n_chunks;           // group / heads_per_wg
     bool balanced;          // route: even split of all token tiles over a resident grid
+    int bal_waves;          // balanced route: waves per workgroup (8, 12 or 16)
+    int spw;                // balanced route: streams a workgroup reads side by side
+    int waves_per_stream;   // balanced route: bal_waves / spw
+    int bands;              // balanced route: (streams per sequence) / spw
     // fixed-partition route
     int partition;          // tokens per partition (multiple of page_size)
     int n_part_max;         // ceil(max_context_length / partition), >= 1

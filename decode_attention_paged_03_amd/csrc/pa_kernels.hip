@@ -2,15 +2,19 @@
 //
 // Two routes over the same per-tile arithmetic:
 //
-//  * Balanced (the default): a resident grid of workgroups splits all token tiles of
-//    the batch evenly -- streams (sequence, KV head, head chunk) laid end to end, each
-//    workgroup taking an equal run of 16-token tiles, its waves equal sub-runs.  A
-//    stream a wave holds entirely is finished there (the single-tile path of the
-//    "paged_attention_v2_pytorch.py" commit page); a stream that crosses waves or
-//    workgroups leaves (max, sum, acc) triples that are combined in LDS or, across
-//    workgroups, by pa_merge_balanced -- the split/merge of the "V4 (Context-axis
-//    parallelism)" section of "[TIL] Optimizing paged attention", with the split points
-//    chosen for balance instead of fixed.
+//  * Balanced (the default): a resident grid, one workgroup per CU, splits all token
+//    tiles of the batch evenly.  A sequence's streams (KV head, head chunk) are grouped in
+//    bands of `spw` streams that are read side by side: the waves of a workgroup take
+//    different streams of the same token range, so that every CU reads all row offsets
+//    of a page (the KV heads of a token sit next to each other) and the memory channels
+//    are loaded evenly.  Bands are laid end to end; workgroup w takes the units
+//    [w N / W, (w+1) N / W) of the N (band, 16-token tile) units, and the waves reading
+//    one stream split that range in equal runs.  A stream that a wave holds entirely is
+//    finished there (the single-tile path of the "paged_attention_v2_pytorch.py" commit
+//    page); pieces of a stream that crosses waves are combined in LDS, and pieces that
+//    cross workgroups leave (max, sum, acc) triples for pa_merge_balanced -- the
+//    split/merge of the "V4 (Context-axis parallelism)" section of "[TIL] Optimizing
+//    paged attention", with the split points chosen for balance instead of fixed.
 //  * Fixed partitions (a partition size or a flag given): one workgroup per (sequence,
 //    KV head, head chunk, partition of partition_size tokens), partition triples in the
 //    workspace, pa_merge_kernel per (sequence, query head) -- p2's PARTITION_SIZE scheme.
@@ -22,28 +26,33 @@
 // The block-table gather follows the "Baseline" and "V3 (Shared memory data reuse)"
 // sections of the first page: token t of a sequence is slot t % page_size of physical
 // page block_tables[b][t / page_size]; one K/V read serves every query head of the GQA
-// group (V3 stages a page in shared memory for this; here the group is scored from
-// registers).  The streaming softmax is that page's Baseline recurrence.
+// group (V3 stages a page in shared memory for this; here both products run on the
+// matrix cores straight from registers).  The streaming softmax is that page's Baseline
+// recurrence.
 //
 // Scores are kept in base-2 units: z = (q . k) * |scale| * log2(e), so every exponential
 // is the hardware exp2 (v_exp_f32).  A negative scale is folded into q (sign flip, exact).
 //
-// Per 16-token tile, one wave does:
-//   Q.K^T  with v_mfma_f32_16x16x32_f16: B = the tile's K rows (lane l holds token l%16,
-//          dims 32j + 8(l/16) .. +7 for MFMA j), A = the query heads, repeated over the
-//          16 MFMA rows so that every lane ends up holding the scores of its column's
-//          token for 4 heads.  This is a dense contraction over head_dim (fp16 products,
-//          fp32 sums), the one place the matrix cores fit this memory-bound path.
-//   softmax: tile max by a DPP max-reduction over the 16 lanes of a row; the reference
-//          max of a head only moves (and the accumulators are rescaled) when a tile's max
-//          exceeds it by more than kRescaleSlack (2^8), so in steady state a tile costs
-//          one exp2 per score and no rescaling.  Any reference value gives the same
-//          final ratio acc / l; the slack only bounds how large the weights may grow.
-//   P.V    on the VALU: the V rows are loaded with D/8 lanes per token (each lane owns
-//          8 dims of the output for every head); the weight of the lane's token is
-//          fetched from the score lanes with ds_bpermute; fma_mix multiplies the fp16
-//          value by the fp32 weight into fp32 accumulators.
-// The next tile's loads (nontemporal, 128-bit) are in flight while a tile is consumed.
+// Per 16-token tile, one wave does (lane l: n = l % 16, g = l / 16):
+//   scores  S^T = K Q^T with v_mfma_f32_16x16x32_f16 over head_dim: A = the tile's K rows
+//           (MFMA row m holds token pi(m) = m / 4 + 4 (m % 4)), B = the query heads of the
+//           chunk (column n = head n, zero past the chunk).  Lane (n, g) then holds the
+//           scores of head n for tokens g, g + 4, g + 8, g + 12.
+//   softmax the reference max of a head only moves (and the accumulators are rescaled)
+//           when a score exceeds it by more than kRescaleSlack (2^8), so in steady state
+//           a tile costs one exp2 per score and no reduction.  Any reference value gives
+//           the same ratio acc / l; the slack only bounds the weights (<= 256, exact
+//           range for fp16).
+//   P.V     with v_mfma_f32_16x16x16_f16: A = the weights rounded to fp16 -- already in
+//           the A layout (lane (n, g) holds head n, tokens g + 4i) -- and B = V.  Lane
+//           (n, g) loads dims E n .. E n + E - 1 (E = D / 16) of rows g, g + 4, g + 8,
+//           g + 12 with one wide load per row (a load instruction covers four whole rows),
+//           and v_perm regroups them into four tokens of one dim; MFMA c takes dims
+//           E n + c.  The weight sum l adds the same rounded weights, so the output is an
+//           exact convex combination of V rows.  Lane (n, g) ends up holding head 4g + i
+//           (register i), dims E n .. E n + E - 1.
+// The next tile's loads (nontemporal) are issued before a tile is consumed when the
+// route prefetches.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -53,7 +62,7 @@
 namespace pa {
 namespace {
 
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
@@ -66,8 +75,13 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 constexpr int kBufferFlags = 0x00020000;
 constexpr int kLoadNontemporal = 2;
 constexpr float kRescaleSlack = 8.0f;   // log2 units
+// byte offset that lies past every tile's buffer range (loads there return zero)
+constexpr uint32_t kOutOfRange = 0x7FFFFF00u;
+#ifndef PA_XCD_REMAP
+#define PA_XCD_REMAP 1   // balanced route: contiguous work per XCD (see xcd_major)
+#endif
 #ifndef PA_BAL_PRIO
-#define PA_BAL_PRIO 1   // balanced route: raise the issue priority of waves that fall behind
+#define PA_BAL_PRIO 1    // balanced route: raise the issue priority of waves that fall behind
 #endif
 
 struct DecodeArgs {
@@ -77,39 +91,15 @@ struct DecodeArgs {
     const int32_t* bt;
     const int32_t* ctx;
     float* out;
-    float* ws_acc;          // [batch][query_heads][n_part_max][D]
-    float* ws_ml;           // [batch][query_heads][n_part_max][2] = (max in log2 units, sum)
-    int4* ws_desc;          // balanced route: per-workgroup merge descriptor
+    float* ws_acc;          // partial rows of D floats
+    float* ws_ml;           // partial rows' (max in log2 units, sum)
+    int4* ws_desc;          // balanced route: per-workgroup merge record
     float scale_log2;       // |scale| * log2(e)
     uint32_t q_sign;        // 0x80008000 to negate q (negative scale), else 0
     int batch, query_heads, kv_heads, group, n_chunks, max_pages, partition, n_part_max, ps_log2;
     int force_split;
+    int spw, waves_per_stream, bands;   // balanced route (see Plan)
 };
-
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-    // every lane has a valid source for the patterns used here, so bound_ctrl does not
-    // matter; it lets the compiler fold the move into the consuming VALU op
-    return __builtin_bit_cast(float,
-                              __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
-}
-
-// All-reduce over each group of 16 consecutive lanes (a DPP row); every lane of the row
-// gets the identical result (partners exchange operands; max and + are commutative).
-__device__ __forceinline__ float row16_max(float x) {
-    x = fmaxf(x, dpp<0xB1>(x));    // quad_perm(1,0,3,2)
-    x = fmaxf(x, dpp<0x4E>(x));    // quad_perm(2,3,0,1)
-    x = fmaxf(x, dpp<0x141>(x));   // row_half_mirror
-    x = fmaxf(x, dpp<0x140>(x));   // row_mirror
-    return x;
-}
-__device__ __forceinline__ float row16_sum(float x) {
-    x += dpp<0xB1>(x);
-    x += dpp<0x4E>(x);
-    x += dpp<0x141>(x);
-    x += dpp<0x140>(x);
-    return x;
-}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -122,81 +112,51 @@ __device__ __forceinline__ void set_wave_priority(int p) {
     else __builtin_amdgcn_s_setprio(0);
 }
 
-__device__ __forceinline__ half8_t as_half8(const uint4& x) {
-    return __builtin_bit_cast(half8_t, x);
-}
+__device__ __forceinline__ half8_t as_half8(const uint4& x) { return __builtin_bit_cast(half8_t, x); }
 
-__device__ __forceinline__ float lo_half(unsigned int w) {
-    return (float)__builtin_bit_cast(half2_t, w).x;
-}
-__device__ __forceinline__ float hi_half(unsigned int w) {
-    return (float)__builtin_bit_cast(half2_t, w).y;
-}
-
-__device__ __forceinline__ float readlane_f(float x, int l) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
-}
-__device__ __forceinline__ float readfirst_f(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
-}
-
-template <int D, int HP>
+template <int D>
 struct Geo {
-    static constexpr int T = 16;           // tokens per wave tile (MFMA N)
-    static constexpr int UK = D / 32;      // K loads (and MFMAs) per tile
-    static constexpr int LR = D / 8;       // lanes per V row
-    static constexpr int NR = 64 / LR;     // V rows (tokens) per load
-    static constexpr int UV = T / NR;      // V loads per tile
-    static constexpr int C4 = D / 4;       // float4 columns of an output row
-    static constexpr int QDUP = HP <= 4 ? 4 : 8;   // MFMA rows i hold head i % QDUP
+    static constexpr int T = 16;          // tokens per wave tile
+    static constexpr int UK = D / 32;     // K loads (and score MFMAs) per tile
+    static constexpr int E = D / 16;      // V dims per lane (fp16), and P.V MFMAs
+    static constexpr int VW = E / 2;      // 32-bit words of a lane's V chunk
+    static constexpr int C4 = D / 4;      // float4 columns of an output row
 };
 
 // Lane coordinates inside a wave.
 struct Lane {
-    int lane, col, grp, vr, vc;
-    template <int D>
+    int lane, n, g;
+    int ktok;   // tile token whose K row this lane loads (MFMA row n)
     __device__ static Lane make(int lane) {
         Lane l;
         l.lane = lane;
-        l.col = lane & 15;       // MFMA column (token within the tile)
-        l.grp = lane >> 4;       // MFMA row group (k-chunk for operands, 4 rows for D)
-        l.vr = lane / (D / 8);   // V row (token within a V load)
-        l.vc = lane % (D / 8);   // V chunk (dims 8vc .. 8vc+7)
+        l.n = lane & 15;
+        l.g = lane >> 4;
+        l.ktok = (l.n >> 2) + 4 * (l.n & 3);
         return l;
     }
 };
 
-// A operand of the score MFMA: head (col % QDUP) of the chunk starting at query row
-// `row0`, dims 32j + 8 grp .. +7; zero past HP heads; sign-flipped for a negative scale.
-// Split into the loads and the fix-up, so that a prefetch does not wait for its data.
+// B operand of the score MFMA: lane (n, g) holds q[row0 + n][32 j + 8 g .. + 7], zero
+// for n >= HP; sign-flipped for a negative scale.  Split into the loads and the fix-up,
+// so that a prefetch does not wait for its data.
 template <int D, int HP>
 __device__ __forceinline__ void load_q_raw(const _Float16* q, size_t row0, const Lane& L,
-                                           uint4 (&qr)[Geo<D, HP>::UK]) {
-    using G = Geo<D, HP>;
-    const int hq = L.col % G::QDUP;
-    const uint4* qp = reinterpret_cast<const uint4*>(q + (row0 + (hq < HP ? hq : 0)) * D);
+                                           uint4 (&qr)[Geo<D>::UK]) {
+    const uint4* qp = reinterpret_cast<const uint4*>(q + (row0 + (L.n < HP ? L.n : 0)) * D);
 #pragma unroll
-    for (int j = 0; j < G::UK; ++j) qr[j] = qp[4 * j + L.grp];
+    for (int j = 0; j < Geo<D>::UK; ++j) qr[j] = qp[4 * j + L.g];
 }
 template <int D, int HP>
-__device__ __forceinline__ void fix_q(const uint4 (&qr)[Geo<D, HP>::UK], uint32_t q_sign, const Lane& L,
-                                      half8_t (&qa)[Geo<D, HP>::UK]) {
-    using G = Geo<D, HP>;
-    const bool used = (L.col % G::QDUP) < HP;
+__device__ __forceinline__ void fix_q(const uint4 (&qr)[Geo<D>::UK], uint32_t q_sign, const Lane& L,
+                                      half8_t (&qb)[Geo<D>::UK]) {
 #pragma unroll
-    for (int j = 0; j < G::UK; ++j) {
+    for (int j = 0; j < Geo<D>::UK; ++j) {
         uint4 w = qr[j];
         w.x ^= q_sign; w.y ^= q_sign; w.z ^= q_sign; w.w ^= q_sign;
-        if (!used) w = uint4{0u, 0u, 0u, 0u};
-        qa[j] = as_half8(w);
+        if (L.n >= HP) w = uint4{0u, 0u, 0u, 0u};
+        qb[j] = as_half8(w);
     }
-}
-template <int D, int HP>
-__device__ __forceinline__ void load_q(const _Float16* q, size_t row0, uint32_t q_sign, const Lane& L,
-                                       half8_t (&qa)[Geo<D, HP>::UK]) {
-    uint4 qr[Geo<D, HP>::UK];
-    load_q_raw<D, HP>(q, row0, L, qr);
-    fix_q<D, HP>(qr, q_sign, L, qa);
 }
 
 // A raw buffer resource over `bytes` bytes at `base`.  Loads past `bytes` return zero
@@ -205,177 +165,185 @@ __device__ __forceinline__ void load_q(const _Float16* q, size_t row0, uint32_t 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* base, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, bytes, kBufferFlags);
 }
-__device__ __forceinline__ uint4 buf_ld(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    const u32x4_t t = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kLoadNontemporal);
+// `off` is the lane's byte offset, `soff` a wave-uniform one (an SGPR operand).
+__device__ __forceinline__ uint4 buf_ld128(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff = 0) {
+    const u32x4_t t = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, (int)soff, kLoadNontemporal);
     return uint4{t.x, t.y, t.z, t.w};
+}
+// VW (2 or 4) words of one lane's V chunk
+template <int VW>
+__device__ __forceinline__ void buf_ldv(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff, uint32_t (&w)[VW]) {
+    if constexpr (VW == 4) {
+        const u32x4_t t = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, (int)soff, kLoadNontemporal);
+        w[0] = t.x; w[1] = t.y; w[2] = t.z; w[3] = t.w;
+    } else {
+        static_assert(VW == 2, "V chunks of 4 or 8 halves");
+        typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+        const u32x2_t t = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, (int)soff, kLoadNontemporal);
+        w[0] = t.x; w[1] = t.y;
+    }
 }
 
 // Loads of one 16-token tile.  `kp`/`vp` point at the K/V row (this KV head) of the
-// tile's first token; with pages of 8 the tile's tokens 8..15 sit in the next page,
-// whose rows start at `kp2`/`vp2`.  Tokens past n_valid (0..16, wave-uniform) read as
-// zero: their scores are masked, and their zero V rows add nothing.
-template <int D, int HP, bool SPLIT>
+// tile's first token; with pages of 8 the tile's tokens 8..15 sit in the next page, whose
+// rows start at `kp2`/`vp2`.  Tokens past n_valid (0..16, wave-uniform) read as zero:
+// their scores are masked, and their zero V rows add nothing.
+//   K: kb[j] = 16 bytes of row ktok, dims 32 j + 8 g .. + 7 (koff = ktok * tok + 16 g).
+//   V: vb[i] = dims E n .. E n + E - 1 of row 4 i + g (voff = g * tok + 2 E n).
+template <int D, bool SPLIT>
 __device__ __forceinline__ void load_kv(const char* kp, const char* vp, const char* kp2, const char* vp2,
-                                        uint32_t koff, const uint32_t (&voff)[Geo<D, HP>::UV],
-                                        uint32_t tok_bytes, int n_valid, const Lane& L,
-                                        uint4 (&kb)[Geo<D, HP>::UK], uint4 (&vb)[Geo<D, HP>::UV]) {
-    using G = Geo<D, HP>;
+                                        uint32_t koff, uint32_t voff, uint32_t tok_bytes, int n_valid,
+                                        const Lane& L, uint4 (&kb)[Geo<D>::UK],
+                                        uint32_t (&vb)[4][Geo<D>::VW]) {
+    using G = Geo<D>;
     n_valid = __builtin_amdgcn_readfirstlane(n_valid);   // uniform; keeps the resource in SGPRs
     if constexpr (!SPLIT) {
         const int bytes = n_valid * (int)tok_bytes;
         const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kp, bytes);
         const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vp, bytes);
 #pragma unroll
-        for (int j = 0; j < G::UK; ++j) kb[j] = buf_ld(rk, koff + 64 * j);
+        for (int j = 0; j < G::UK; ++j) kb[j] = buf_ld128(rk, koff + 64 * j);
 #pragma unroll
-        for (int u = 0; u < G::UV; ++u) vb[u] = buf_ld(rv, voff[u]);
+        for (int i = 0; i < 4; ++i) buf_ldv<G::VW>(rv, voff, 4 * i * tok_bytes, vb[i]);
     } else {
         const int n1 = min(n_valid, 8), n2 = max(n_valid - 8, 0);
         const __amdgpu_buffer_rsrc_t rk1 = tile_rsrc(kp, n1 * (int)tok_bytes);
         const __amdgpu_buffer_rsrc_t rk2 = tile_rsrc(kp2, n2 * (int)tok_bytes);
         const __amdgpu_buffer_rsrc_t rv1 = tile_rsrc(vp, n1 * (int)tok_bytes);
         const __amdgpu_buffer_rsrc_t rv2 = tile_rsrc(vp2, n2 * (int)tok_bytes);
-        // Columns 0..7 read the first page, 8..15 the next one.  Both loads are issued by
-        // every lane with a wave-uniform resource; the lane's offset into the page it does
-        // not use is pushed past the resource's range, so that load returns zero and the
-        // two results combine with an OR.
-        const uint32_t k1 = (L.col < 8) ? koff : 0x7FFFFF00u;
-        const uint32_t k2 = (L.col < 8) ? 0x7FFFFF00u : koff - 8 * tok_bytes;
+        // K rows 0..7 are in the first page, 8..15 in the next.  Both loads are issued by
+        // every lane with a wave-uniform resource; the lane's offset into the page it
+        // does not use is pushed past the resource's range, so that load returns zero and
+        // the two results combine with an OR.
+        const bool first = L.ktok < 8;
+        const uint32_t k1 = first ? koff : kOutOfRange;
+        const uint32_t k2 = first ? kOutOfRange : koff - 8 * tok_bytes;
 #pragma unroll
         for (int j = 0; j < G::UK; ++j) {
-            const uint4 x = buf_ld(rk1, k1 + 64 * j);
-            const uint4 y = buf_ld(rk2, k2 + 64 * j);
+            const uint4 x = buf_ld128(rk1, k1 + 64 * j);
+            const uint4 y = buf_ld128(rk2, k2 + 64 * j);
             kb[j] = uint4{x.x | y.x, x.y | y.y, x.z | y.z, x.w | y.w};
         }
+        // V group i covers rows 4 i .. 4 i + 3: groups 0, 1 in the first page, 2, 3 in the next
 #pragma unroll
-        for (int u = 0; u < G::UV; ++u) {
-            // V load u covers tile rows u*NR .. u*NR+NR-1, all in one page (NR divides 8)
-            if (u * G::NR < 8) vb[u] = buf_ld(rv1, voff[u]);
-            else vb[u] = buf_ld(rv2, voff[u] - 8 * tok_bytes);
+        for (int i = 0; i < 4; ++i) {
+            if (i < 2) buf_ldv<G::VW>(rv1, voff, 4 * i * tok_bytes, vb[i]);
+            else buf_ldv<G::VW>(rv2, voff, (4 * i - 8) * tok_bytes, vb[i]);
         }
     }
 }
 
-// Streaming softmax state of one wave for HP heads: a reference max per head, kept both
-// wave-uniform (mref, for the V layout) and per lane in the score layout (mrow[e] = mref
-// of the head in score register e of this lane's row group); running sums in the score
-// layout; output accumulators in the V layout (8 dims per lane per head).
+// Streaming softmax state of one wave for HP (<= 8) heads.  Lane (n, g): mref = reference
+// max of head n (equal on the four lanes of a head), lsum = this lane's share of head n's
+// weight sum, acc[c][i] = output of head 4 g + i, dim E n + c.
 template <int D, int HP>
 struct WaveState {
-    using G = Geo<D, HP>;
-    float mref[HP];
-    float mrow[4];
-    float lsum[4];
-    float acc[HP][8];
+    using G = Geo<D>;
+    float mref;
+    float lsum;
+    float4_t acc[G::E];
 
     __device__ __forceinline__ void reset() {
+        mref = -INFINITY;
+        lsum = 0.f;
 #pragma unroll
-        for (int h = 0; h < HP; ++h) {
-            mref[h] = -INFINITY;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) acc[h][j] = 0.f;
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            mrow[e] = -INFINITY;
-            lsum[e] = 0.f;
-        }
+        for (int c = 0; c < G::E; ++c) acc[c] = float4_t{0.f, 0.f, 0.f, 0.f};
     }
 
-    // One tile: tokens with col >= n_valid are masked (n_valid in 0..16, wave-uniform).
-    __device__ __forceinline__ void tile(const half8_t (&qa)[G::UK], const uint4 (&kb)[G::UK],
-                                         const uint4 (&vb)[G::UV], int n_valid, float sl2, const Lane& L) {
+    // One tile: tokens at or past n_valid are masked (n_valid in 1..16, wave-uniform).
+    __device__ __forceinline__ void tile(const half8_t (&qb)[G::UK], const uint4 (&kb)[G::UK],
+                                         const uint32_t (&vb)[4][G::VW], int n_valid, float sl2,
+                                         const Lane& L) {
         float4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < G::UK; ++j)
-            s = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[j], as_half8(kb[j]), s, 0, 0, 0);
-        const bool valid = L.col < n_valid;
-        float z[4], zt[4];
+        for (int j = 0; j < G::UK; ++j) s = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(kb[j]), qb[j], s, 0, 0, 0);
+        // register i: token g + 4 i of head n
+        float z[4];
         bool grow = false;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            z[e] = valid ? s[e] * sl2 : -INFINITY;
-            zt[e] = row16_max(z[e]);
-            grow |= zt[e] > mrow[e] + kRescaleSlack;
+        for (int i = 0; i < 4; ++i) {
+            z[i] = (L.g + 4 * i < n_valid) ? s[i] * sl2 : -INFINITY;
+            grow |= z[i] > mref + kRescaleSlack;
         }
+        grow = grow && L.n < HP;
         if (__builtin_amdgcn_ballot_w64(grow) != 0) {   // rare: move the reference max
-            float mt[HP];
+            // token 0 is valid, so every head's tile maximum is finite
+            float zt = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+            zt = fmaxf(zt, __shfl_xor(zt, 16));
+            zt = fmaxf(zt, __shfl_xor(zt, 32));
+            const float mn = fmaxf(mref, zt);
+            const float alpha = fast_exp2(mref - mn);   // 0 while mref is -inf
+            mref = mn;
+            lsum *= alpha;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                if (e < HP) mt[e] = readfirst_f(zt[e]);
-                if (HP > 4 && e + 4 < HP) mt[e + 4] = readlane_f(zt[e], 16);
-            }
-            float alpha[HP];
+            for (int i = 0; i < 4; ++i) {
+                const float ai = __shfl(alpha, 4 * L.g + i);   // head 4 g + i
 #pragma unroll
-            for (int h = 0; h < HP; ++h) {
-                const float mn = fmaxf(mref[h], mt[h]);
-                alpha[h] = fast_exp2(mref[h] - mn);    // 0 when mref was -inf
-                mref[h] = mn;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) acc[h][j] *= alpha[h];
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                if constexpr (HP <= 4) {
-                    if (e < HP) {
-                        lsum[e] *= alpha[e];
-                        mrow[e] = mref[e];
-                    }
-                } else {
-                    const bool hi = (L.grp & 1) != 0;
-                    if (e + 4 < HP) {
-                        lsum[e] *= hi ? alpha[e + 4] : alpha[e];
-                        mrow[e] = hi ? mref[e + 4] : mref[e];
-                    } else {
-                        lsum[e] *= hi ? 1.f : alpha[e];
-                        mrow[e] = hi ? 0.f : mref[e];
-                    }
-                }
+                for (int c = 0; c < G::E; ++c) acc[c][i] *= ai;
             }
         }
-        // weights in the score layout (rows of heads past HP carry unused values)
-        float p[4];
+        half4_t p;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            p[e] = fast_exp2(z[e] - mrow[e]);
-            lsum[e] += p[e];
+        for (int i = 0; i < 4; ++i) {
+            p[i] = (_Float16)fast_exp2(z[i] - mref);
+            lsum += (float)p[i];
         }
-        // P.V: lane (vr, vc) takes the weight of tile token u*NR + vr from its score lane
+        // B operand of P.V for dim E n + c: tokens g, g + 4, g + 8, g + 12 (half c of
+        // the rows' chunks)
 #pragma unroll
-        for (int u = 0; u < G::UV; ++u) {
-            float f[8];
-            f[0] = lo_half(vb[u].x); f[1] = hi_half(vb[u].x);
-            f[2] = lo_half(vb[u].y); f[3] = hi_half(vb[u].y);
-            f[4] = lo_half(vb[u].z); f[5] = hi_half(vb[u].z);
-            f[6] = lo_half(vb[u].w); f[7] = hi_half(vb[u].w);
+        for (int j = 0; j < G::VW; ++j) {
+            const uint32_t w0 = vb[0][j], w1 = vb[1][j], w2 = vb[2][j], w3 = vb[3][j];
+            const uint2 even = {__builtin_amdgcn_perm(w1, w0, 0x05040100u), __builtin_amdgcn_perm(w3, w2, 0x05040100u)};
+            const uint2 odd = {__builtin_amdgcn_perm(w1, w0, 0x07060302u), __builtin_amdgcn_perm(w3, w2, 0x07060302u)};
+            acc[2 * j] = __builtin_amdgcn_mfma_f32_16x16x16f16(p, __builtin_bit_cast(half4_t, even), acc[2 * j], 0, 0, 0);
+            acc[2 * j + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(p, __builtin_bit_cast(half4_t, odd), acc[2 * j + 1], 0, 0, 0);
+        }
+    }
+
+    // Weight sum of head n (returned on every lane of head n).  All lanes must call it.
+    __device__ __forceinline__ float head_sum() const {
+        float l = lsum;
+        l += __shfl_xor(l, 16);
+        l += __shfl_xor(l, 32);
+        return l;
+    }
+
+    // Visit this lane's output values: f(head, dim, float4 at dims dim .. dim + 3, i).
+    template <typename F>
+    __device__ __forceinline__ void for_each_out(const Lane& L, F&& f) const {
 #pragma unroll
-            for (int h = 0; h < HP; ++h) {
-                const int src_grp = (HP <= 4) ? L.grp : (h >> 2);
-                const int src = u * G::NR + L.vr + 16 * src_grp;
-                const float w = __builtin_bit_cast(
-                    float, __builtin_amdgcn_ds_bpermute(src * 4, __builtin_bit_cast(int, p[h & 3])));
+        for (int i = 0; i < 4; ++i) {
+            const int hh = 4 * L.g + i;
+            if (hh < HP) {
 #pragma unroll
-                for (int j = 0; j < 8; ++j) acc[h][j] = fmaf(w, f[j], acc[h][j]);
+                for (int c = 0; c < G::E; c += 4)
+                    f(hh, G::E * L.n + c, float4_t{acc[c][i], acc[c + 1][i], acc[c + 2][i], acc[c + 3][i]}, i);
             }
         }
     }
 
-    // Sums over the 16 score columns (wave-uniform l per head) and over the V rows
-    // (acc in place; every row then holds the full sums).
-    __device__ __forceinline__ void reduce(float (&lw)[HP]) {
+    // Write the finished rows out[row0 + h] = acc / l for h < HP.  All lanes must call it.
+    __device__ __forceinline__ void write_out(float* out, size_t row0, const Lane& L) const {
+        const float l = head_sum();
+        float rl[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float r = row16_sum(lsum[e]);
-            if (e < HP) lw[e] = readfirst_f(r);
-            if (HP > 4 && e + 4 < HP) lw[e + 4] = readlane_f(r, 16);
+        for (int i = 0; i < 4; ++i) rl[i] = 1.f / __shfl(l, 4 * L.g + i);
+        for_each_out(L, [&](int hh, int dim, float4_t v, int i) {
+            *reinterpret_cast<float4_t*>(out + (row0 + hh) * D + dim) = v * rl[i];
+        });
+    }
+
+    // Store the unnormalised triple: m[h], l[h], acc[h * D + dim] for h < HP.  All lanes
+    // must call it.
+    __device__ __forceinline__ void store_triple(float* m, float* l_out, float* accp, const Lane& L) const {
+        const float l = head_sum();
+        if (L.g == 0 && L.n < HP) {
+            m[L.n] = mref;
+            l_out[L.n] = l;
         }
-#pragma unroll
-        for (int off = G::LR; off < 64; off <<= 1) {
-#pragma unroll
-            for (int h = 0; h < HP; ++h)
-#pragma unroll
-                for (int j = 0; j < 8; ++j) acc[h][j] += __shfl_xor(acc[h][j], off);
-        }
+        for_each_out(L, [&](int hh, int dim, float4_t v, int) {
+            *reinterpret_cast<float4_t*>(accp + hh * D + dim) = v;
+        });
     }
 };
 
@@ -389,7 +357,7 @@ struct WaveState {
 template <int D, int HP, int DEPTH, int NW, bool SPLIT>
 __global__ void __launch_bounds__(NW * 64)
 pa_decode_kernel(DecodeArgs a) {
-    using G = Geo<D, HP>;
+    using G = Geo<D>;
     constexpr int T = G::T;
     constexpr int C4 = G::C4;
 
@@ -400,7 +368,7 @@ pa_decode_kernel(DecodeArgs a) {
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const Lane L = Lane::make<D>(tid & 63);
+    const Lane L = Lane::make(tid & 63);
 
     // Work item: partitions vary slowest, so every sequence's first (largest) partition
     // is dispatched before any remainder partition.
@@ -434,18 +402,20 @@ pa_decode_kernel(DecodeArgs a) {
     const int32_t* bt_row = a.bt + (size_t)b * a.max_pages + pg0;
     for (int i = tid; i < npg; i += NW * 64) s_bt[i] = bt_row[i];
 
-    half8_t qa[G::UK];
-    load_q<D, HP>(a.q, row0, a.q_sign, L, qa);
+    half8_t qb[G::UK];
+    {
+        uint4 qr[G::UK];
+        load_q_raw<D, HP>(a.q, row0, L, qr);
+        fix_q<D, HP>(qr, a.q_sign, L, qb);
+    }
     __syncthreads();
 
     const size_t tok_bytes = (size_t)a.kv_heads * D * 2;     // bytes between slots
     const size_t page_bytes = tok_bytes << ps_log2;
     const char* kbase = a.k + (size_t)kvh * D * 2;
     const char* vbase = a.v + (size_t)kvh * D * 2;
-    const uint32_t koff = (uint32_t)(L.col * tok_bytes) + 16u * L.grp;   // + 64 j
-    uint32_t voff[G::UV];
-#pragma unroll
-    for (int u = 0; u < G::UV; ++u) voff[u] = (uint32_t)((u * G::NR + L.vr) * tok_bytes) + 16u * L.vc;
+    const uint32_t koff = (uint32_t)(L.ktok * tok_bytes) + 16u * L.g;
+    const uint32_t voff = (uint32_t)(L.g * tok_bytes) + 2u * G::E * L.n;
     const float sl2 = a.scale_log2;
 
     WaveState<D, HP> st;
@@ -456,7 +426,7 @@ pa_decode_kernel(DecodeArgs a) {
     // This wave takes tiles wave, wave + NW, ...
     const int nk = wave < n_tiles ? (n_tiles - wave + NW - 1) / NW : 0;
 
-    auto load_tile = [&](int k, uint4 (&kb)[G::UK], uint4 (&vb)[G::UV]) {
+    auto load_tile = [&](int k, uint4 (&kb)[G::UK], uint32_t (&vb)[4][G::VW]) {
         const int t0 = t_begin + (wave + k * NW) * T;
         const int pg = (t0 >> ps_log2) - pg0;
         const int phys = __builtin_amdgcn_readfirstlane(s_bt[pg]);
@@ -467,8 +437,8 @@ pa_decode_kernel(DecodeArgs a) {
             // tile reaches past token 8
             if (t0 + 8 < t_end) base2 = (size_t)__builtin_amdgcn_readfirstlane(s_bt[pg + 1]) * page_bytes;
         }
-        load_kv<D, HP, SPLIT>(kbase + base, vbase + base, kbase + base2, vbase + base2, koff, voff,
-                              (uint32_t)tok_bytes, max(0, min(T, t_end - t0)), L, kb, vb);
+        load_kv<D, SPLIT>(kbase + base, vbase + base, kbase + base2, vbase + base2, koff, voff,
+                          (uint32_t)tok_bytes, max(0, min(T, t_end - t0)), L, kb, vb);
     };
 
     if (nk > 0) {
@@ -476,10 +446,11 @@ pa_decode_kernel(DecodeArgs a) {
         // The loop runs a multiple of DEPTH tiles and has no exit in its middle, so the
         // compiler's wait-count bookkeeping sees the same outstanding loads on every path
         // into the loop header.  Padding tiles (k >= nk) reload the last tile (already in
-        // the caches) and are fully masked, which leaves the state unchanged.  The
-        // scheduling barriers keep the compiler from sinking the loads below the
-        // arithmetic of the tile before them.
-        uint4 kb[DEPTH][G::UK], vb[DEPTH][G::UV];
+        // the caches) and are skipped after their loads are waited for.  The scheduling
+        // barriers keep the compiler from sinking the loads below the arithmetic of the
+        // tile before them.
+        uint4 kb[DEPTH][G::UK];
+        uint32_t vb[DEPTH][4][G::VW];
 #pragma unroll
         for (int d = 0; d < DEPTH - 1; ++d) load_tile(min(d, nk - 1), kb[d], vb[d]);
         for (int k = 0; k < nk; k += DEPTH) {
@@ -489,24 +460,13 @@ pa_decode_kernel(DecodeArgs a) {
                 load_tile(min(k + d + DEPTH - 1, nk - 1), kb[nxt], vb[nxt]);
                 __builtin_amdgcn_sched_barrier(0);
                 const int t0 = t_begin + (wave + (k + d) * NW) * T;
-                st.tile(qa, kb[d], vb[d], max(0, min(T, t_end - t0)), sl2, L);
+                if (k + d < nk) st.tile(qb, kb[d], vb[d], max(0, min(T, t_end - t0)), sl2, L);
+                else __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
             }
         }
     }
 
-    float lw[HP];
-    st.reduce(lw);
-    if (L.lane < G::LR) {
-#pragma unroll
-        for (int h = 0; h < HP; ++h) {
-            s_acc[wave][h][2 * L.vc] = float4_t{st.acc[h][0], st.acc[h][1], st.acc[h][2], st.acc[h][3]};
-            s_acc[wave][h][2 * L.vc + 1] = float4_t{st.acc[h][4], st.acc[h][5], st.acc[h][6], st.acc[h][7]};
-            if (L.lane == 0) {
-                s_m[wave][h] = st.mref[h];
-                s_l[wave][h] = lw[h];
-            }
-        }
-    }
+    st.store_triple(&s_m[wave][0], &s_l[wave][0], reinterpret_cast<float*>(&s_acc[wave][0][0]), L);
     __syncthreads();
 
     // Combine the NW wave states; wave 0 saw token t_begin, so M is finite and waves
@@ -555,7 +515,7 @@ constexpr int kMergeThreads = 256;
 // r(p) = row_rest + (p - 1) * stride.  One pass: thread (g, c) folds the triples
 // p = g, g + GR, ... for float4 column c into a running triple, rescaling whenever its
 // maximum grows; the GR partial triples are then combined through LDS.  Every thread of
-// the block takes part.  Every triple has a finite maximum (it covers >= 1 token).
+// the block takes part.  At least one triple has a finite maximum.
 template <int D>
 __device__ __forceinline__ void combine_rows(const float* ws_ml, const float* ws_acc, size_t row_first,
                                              size_t row_rest, size_t stride, int n, float* out_row) {
@@ -640,12 +600,13 @@ pa_merge_kernel(MergeArgs a) {
 // ------------------------------------------------------------------------------------
 // Balanced route: one resident workgroup per CU splits all token tiles evenly.
 //
-// A stream is one (sequence b, KV head, head chunk): ceil(ctx_b / 16) tiles.  The
-// streams are laid end to end in the order (b, KV head, chunk); workgroup w takes the
-// tiles [w N / W, (w+1) N / W) of the N in total, and its NW waves split that range into
-// NW contiguous pieces.  A wave walks its piece tile by tile across stream boundaries,
-// with one tile (or DEPTH - 1 tiles ahead) in flight: many waves per CU, each with little
-// in flight, keep the memory system fuller than few waves with deep queues.
+// Streams of a sequence: s = kv_head * n_chunks + chunk, S of them.  They are grouped in
+// bands of spw consecutive streams (band = s / spw); a unit is (sequence b, band, tile lt)
+// and the units are laid end to end in the order (b, band, lt), N in total.  Workgroup w
+// takes the units [w N / W, (w+1) N / W).  Its waves form spw groups of
+// waves_per_stream: wave (sp, r) reads stream band * spw + sp of every unit in the r-th
+// equal run of the workgroup's range, crossing band and sequence boundaries as the units
+// do, one tile (or one tile ahead) at a time.
 // A stream that lies wholly inside one wave is finished by that wave (the single-pass
 // case); pieces of a stream that crosses waves are combined in LDS at the end of the
 // workgroup, and a stream that crosses workgroups leaves one (max, sum, acc) triple per
@@ -653,7 +614,7 @@ pa_merge_kernel(MergeArgs a) {
 // ------------------------------------------------------------------------------------
 
 // Lengths -> LDS, exclusive prefix sums of tiles per sequence.  Every thread of the
-// block calls it; returns the total tile count of one (KV head, chunk) plane.
+// block calls it; returns the total tile count of one band plane.
 template <int NT>
 __device__ __forceinline__ int tile_prefix(const int32_t* ctx, int B, int* s_pref, int* s_ctx, int* s_wsum) {
     const int tid = threadIdx.x;
@@ -694,21 +655,30 @@ __device__ __forceinline__ int tile_prefix(const int32_t* ctx, int B, int* s_pre
     return total;
 }
 
-// Stream position of global tile t (0 <= t < N): sequence b (the smallest with
-// KC * pref[b+1] > t), stream index within the sequence sidx = kvh * n_chunks + chunk,
-// tile lt in the stream.  The host keeps N below 2^31.
-__device__ __forceinline__ void locate_tile(int t, int B, int KC, const int* s_pref, int& b, int& sidx, int& lt) {
+// Position of unit t (0 <= t < N): sequence b (the smallest with SG * pref[b+1] > t),
+// band within the sequence, tile lt of the band.  The host keeps N below 2^31.
+__device__ __forceinline__ void locate_unit(int t, int B, int SG, const int* s_pref, int& b, int& band, int& lt) {
     int lo = 0, hi = B - 1;
     while (lo < hi) {
         const int mid = (lo + hi) >> 1;
-        if (KC * s_pref[mid + 1] > t) hi = mid;
+        if (SG * s_pref[mid + 1] > t) hi = mid;
         else lo = mid + 1;
     }
     b = lo;
     const int Tb = s_pref[b + 1] - s_pref[b];
-    const int off = t - KC * s_pref[b];
-    sidx = off / Tb;
-    lt = off - sidx * Tb;
+    const int off = t - SG * s_pref[b];
+    band = off / Tb;
+    lt = off - band * Tb;
+}
+
+// Workgroups are handed to the XCDs in turn (workgroup i to XCD i % kXcds), and each XCD
+// has its own L2.  This renumbering gives each XCD a contiguous run of the work, so that
+// the pieces of a stream split between workgroups mostly meet in one L2.
+// A bijection of [0, G): XCD x's k-th workgroup becomes x * (G / X) + min(x, G % X) + k.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_major(int b, int G) {
+    const int x = b % kXcds, k = b / kXcds, q = G / kXcds, r = G % kXcds;
+    return x * q + min(x, r) + k;
 }
 
 // floor(x * N / W) for 0 <= x <= W.  Exact in double: x N < 2^53 is represented exactly,
@@ -718,10 +688,17 @@ __device__ __forceinline__ int split_point(int x, int N, int W) {
     return (int)floor((double)x * (double)N / (double)W);
 }
 
+// The workgroup holding unit c (0 <= c < N): the largest x with split_point(x) <= c,
+// i.e. floor(((c + 1) W - 1) / N) (exact in double, as for split_point).
+__device__ __forceinline__ int wg_of_unit(int c, int N, int W) {
+    const int x = (int)floor((((double)c + 1.0) * (double)W - 1.0) / (double)N);
+    return min(x, W - 1);
+}
+
 template <int D, int HP, int DEPTH, int NW, bool SPLIT>
 __global__ void __launch_bounds__(NW * 64)
 pa_decode_balanced(DecodeArgs a) {
-    using G = Geo<D, HP>;
+    using G = Geo<D>;
     constexpr int T = G::T;
     constexpr int C4 = G::C4;
     constexpr int NT = NW * 64;
@@ -733,7 +710,7 @@ pa_decode_balanced(DecodeArgs a) {
     __shared__ float s_m[NS][HP];
     __shared__ float s_l[NS][HP];
     __shared__ float4_t s_acc[NS][HP][C4];
-    __shared__ int s_meta[NS][3];    // stream id (-1: empty), first tile, end tile (global)
+    __shared__ int s_meta[NS][3];    // stream id (-1: empty), first unit, end unit
     __shared__ int s_runs[NS + 1];   // first slot of each run of one stream's slots, then NS
     __shared__ int s_nruns;
 
@@ -742,7 +719,14 @@ pa_decode_balanced(DecodeArgs a) {
     int* s_ctx = s_dyn + B + 1;      // [B]
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const Lane L = Lane::make<D>(tid & 63);
+    const Lane L = Lane::make(tid & 63);
+
+    const int SPW = a.spw;                    // streams side by side
+    const int RW = a.waves_per_stream;        // waves per stream
+    const int SG = a.bands;                   // bands per sequence
+    const int S = SG * SPW;                   // streams per sequence
+    const int sp = wave / RW;                 // this wave's stream within a band
+    const int rr = wave - sp * RW;            // this wave's run of the workgroup's range
 
     if (tid < NS) s_meta[tid][0] = -1;
     const int plane = tile_prefix<NT>(a.ctx, B, s_pref, s_ctx, s_wsum);
@@ -752,33 +736,30 @@ pa_decode_balanced(DecodeArgs a) {
         if (s_ctx[b] == 0)
             for (int i = tid; i < a.query_heads * D; i += NT) a.out[(size_t)b * a.query_heads * D + i] = 0.f;
 
-    const int KC = a.kv_heads * a.n_chunks;
-    const int N = KC * plane;
+    const int N = SG * plane;
     const int NWG = gridDim.x;
-    const int w = blockIdx.x;
+    const int w = PA_XCD_REMAP ? xcd_major((int)blockIdx.x, NWG) : (int)blockIdx.x;
     const int g0 = split_point(w, N, NWG);
     const int g1 = split_point(w + 1, N, NWG);
-    const int wr0 = g0 + (int)((long long)(g1 - g0) * wave / NW);
-    const int wr1 = g0 + (int)((long long)(g1 - g0) * (wave + 1) / NW);
+    const int wr0 = g0 + (int)((long long)(g1 - g0) * rr / RW);
+    const int wr1 = g0 + (int)((long long)(g1 - g0) * (rr + 1) / RW);
     const int nk = wr1 - wr0;
 
     const int ps_log2 = a.ps_log2;
     const size_t tok_bytes = (size_t)a.kv_heads * D * 2;
     const size_t page_bytes = tok_bytes << ps_log2;
-    const uint32_t koff = (uint32_t)(L.col * tok_bytes) + 16u * L.grp;   // + 64 j
-    uint32_t voff[G::UV];
-#pragma unroll
-    for (int u = 0; u < G::UV; ++u) voff[u] = (uint32_t)((u * G::NR + L.vr) * tok_bytes) + 16u * L.vc;
+    const uint32_t koff = (uint32_t)(L.ktok * tok_bytes) + 16u * L.g;
+    const uint32_t voff = (uint32_t)(L.g * tok_bytes) + 2u * G::E * L.n;
     const float sl2 = a.scale_log2;
 
-    // Physical pages of the wave's tiles, 64 at a time: lane i holds the page of tile
+    // Physical pages of the wave's units, 64 at a time: lane i holds the page of unit
     // (wr0 + batch + i) (and, for pages of 8, the page of its second half).
     int btv = 0, btv2 = 0;
     auto load_pages = [&](int batch) {
         const int t = wr0 + batch + L.lane;
         if (t < wr1) {
-            int b, sidx, lt;
-            locate_tile(t, B, KC, s_pref, b, sidx, lt);
+            int b, band, lt;
+            locate_unit(t, B, SG, s_pref, b, band, lt);
             const int tok = lt * T;
             const int32_t* row = a.bt + (size_t)b * a.max_pages;
             btv = row[tok >> ps_log2];
@@ -791,48 +772,52 @@ pa_decode_balanced(DecodeArgs a) {
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     };
 
-    // A wave-uniform cursor over the tiles to load, and the description of a loaded tile.
+    // A wave-uniform cursor over the units to load, and the description of a loaded tile.
     struct Desc {
-        int b, sidx, lt, T, n_valid;
+        int b, s, lt, T, n_valid;
         bool first;   // the tile opens a segment of this wave (its first, or a stream start)
     };
-    // cursor: sequence cb, stream index cs, tile cl of cT tiles, sequence length cctx,
-    // KV head ckvh of the stream (all wave-uniform)
-    int cb = 0, cs = 0, cl = 0, cT = 1, cctx = 0, ckvh = 0;
+    // cursor: sequence cb, band cband, tile cl of cT tiles, sequence length cctx; stream
+    // cs = cband * SPW + sp, its KV head ckvh and head chunk cchunk (all wave-uniform)
+    int cb = 0, cband = 0, cl = 0, cT = 1, cctx = 0, cs = 0, ckvh = 0, cchunk = 0;
+    auto set_stream = [&]() {
+        cs = cband * SPW + sp;
+        ckvh = cs / a.n_chunks;
+        cchunk = cs - ckvh * a.n_chunks;
+    };
     if (nk > 0) {
-        locate_tile(wr0, B, KC, s_pref, cb, cs, cl);
+        locate_unit(wr0, B, SG, s_pref, cb, cband, cl);
         cb = __builtin_amdgcn_readfirstlane(cb);
-        cs = __builtin_amdgcn_readfirstlane(cs);
+        cband = __builtin_amdgcn_readfirstlane(cband);
         cl = __builtin_amdgcn_readfirstlane(cl);
         cT = __builtin_amdgcn_readfirstlane(s_pref[cb + 1] - s_pref[cb]);
         cctx = __builtin_amdgcn_readfirstlane(s_ctx[cb]);
-        ckvh = cs / a.n_chunks;
+        set_stream();
         load_pages(0);
     }
     auto advance = [&]() {
         if (++cl == cT) {
             cl = 0;
-            if (++cs == KC) {
-                cs = 0;
+            if (++cband == SG) {
+                cband = 0;
                 do {
                     ++cb;
                 } while (cb < B && s_pref[cb + 1] == s_pref[cb]);
-                if (cb >= B) cb = B - 1;    // past the last tile; never loaded
+                if (cb >= B) cb = B - 1;    // past the last unit; never loaded
                 cT = __builtin_amdgcn_readfirstlane(s_pref[cb + 1] - s_pref[cb]);
                 cctx = __builtin_amdgcn_readfirstlane(s_ctx[cb]);
             }
-            ckvh = cs / a.n_chunks;
+            set_stream();
         }
     };
     // Load tile i of the wave (i < nk) with the cursor at it into (kb, vb); when it opens
-    // a segment, the segment's query rows come with it (into qb), so a new stream costs
+    // a segment, the segment's query rows come with it (into qr), so a new stream costs
     // no extra round trip.
-    auto load_tile = [&](int i, Desc& d, uint4 (&kb)[G::UK], uint4 (&vb)[G::UV], uint4 (&qb)[G::UK]) {
+    auto load_tile = [&](int i, Desc& d, uint4 (&kb)[G::UK], uint32_t (&vb)[4][G::VW], uint4 (&qr)[G::UK]) {
         if ((i & 63) == 0 && i > 0) load_pages(i);
-        const int kvh = ckvh;
         const int tok = cl * T;
         d.b = cb;
-        d.sidx = cs;
+        d.s = cs;
         d.lt = cl;
         d.T = cT;
         d.n_valid = min(T, cctx - tok);
@@ -841,66 +826,44 @@ pa_decode_balanced(DecodeArgs a) {
         const size_t base = (size_t)phys * page_bytes + (size_t)(tok & ((1 << ps_log2) - 1)) * tok_bytes;
         size_t base2 = base;
         if constexpr (SPLIT) base2 = (size_t)__builtin_amdgcn_readlane(btv2, i & 63) * page_bytes;
-        const char* kbase = a.k + (size_t)kvh * D * 2;
-        const char* vbase = a.v + (size_t)kvh * D * 2;
-        load_kv<D, HP, SPLIT>(kbase + base, vbase + base, kbase + base2, vbase + base2, koff, voff,
-                              (uint32_t)tok_bytes, d.n_valid, L, kb, vb);
-        if (d.first) {
-            const int chunk = cs - kvh * a.n_chunks;
-            load_q_raw<D, HP>(a.q, (size_t)cb * a.query_heads + kvh * a.group + chunk * HP, L, qb);
-        }
+        const char* kbase = a.k + (size_t)ckvh * D * 2;
+        const char* vbase = a.v + (size_t)ckvh * D * 2;
+        load_kv<D, SPLIT>(kbase + base, vbase + base, kbase + base2, vbase + base2, koff, voff,
+                          (uint32_t)tok_bytes, d.n_valid, L, kb, vb);
+        if (d.first) load_q_raw<D, HP>(a.q, (size_t)cb * a.query_heads + ckvh * a.group + cchunk * HP, L, qr);
     };
 
     WaveState<D, HP> st;
-    half8_t qa[G::UK];
+    half8_t qb[G::UK];
     int seg_lt0 = 0;       // first stream tile of the open segment
     int seg_i0 = 0;        // first wave tile of the open segment
-    auto consume = [&](const Desc& d, const uint4 (&kb)[G::UK], const uint4 (&vb)[G::UV],
-                       const uint4 (&qb)[G::UK], int i) {
+    auto consume = [&](const Desc& d, const uint4 (&kb)[G::UK], const uint32_t (&vb)[4][G::VW],
+                       const uint4 (&qr)[G::UK], int i) {
         if (d.first) {   // a new segment: its query rows and a fresh state
-            fix_q<D, HP>(qb, a.q_sign, L, qa);
+            fix_q<D, HP>(qr, a.q_sign, L, qb);
             seg_lt0 = d.lt;
             seg_i0 = i;
             st.reset();
         }
-        st.tile(qa, kb, vb, d.n_valid, sl2, L);
+        st.tile(qb, kb, vb, d.n_valid, sl2, L);
         if (d.lt == d.T - 1 || i == nk - 1) {   // the segment ends here
-            const int kvh = d.sidx / a.n_chunks;
-            const int chunk = d.sidx - kvh * a.n_chunks;
+            const int kvh = d.s / a.n_chunks;
+            const int chunk = d.s - kvh * a.n_chunks;
             const size_t row0 = (size_t)d.b * a.query_heads + kvh * a.group + chunk * HP;
-            float lw[HP];
-            st.reduce(lw);
             if (seg_lt0 == 0 && d.lt == d.T - 1) {
-                // the whole stream: finish it
-                if (L.lane < G::LR) {
-#pragma unroll
-                    for (int h = 0; h < HP; ++h) {
-                        float4_t* o = reinterpret_cast<float4_t*>(a.out + (row0 + h) * D) + 2 * L.vc;
-                        const float r = 1.f / lw[h];
-                        o[0] = float4_t{st.acc[h][0], st.acc[h][1], st.acc[h][2], st.acc[h][3]} * r;
-                        o[1] = float4_t{st.acc[h][4], st.acc[h][5], st.acc[h][6], st.acc[h][7]} * r;
-                    }
-                }
+                st.write_out(a.out, row0, L);   // the whole stream: finish it
             } else {
                 // a piece of a stream that continues in another wave: slot 2 wave for the
                 // wave's first segment, 2 wave + 1 for its last one
                 const int slot = 2 * wave + (seg_i0 == 0 ? 0 : 1);
-                if (L.lane < G::LR) {
-#pragma unroll
-                    for (int h = 0; h < HP; ++h) {
-                        s_acc[slot][h][2 * L.vc] = float4_t{st.acc[h][0], st.acc[h][1], st.acc[h][2], st.acc[h][3]};
-                        s_acc[slot][h][2 * L.vc + 1] = float4_t{st.acc[h][4], st.acc[h][5], st.acc[h][6], st.acc[h][7]};
-                    }
-                    if (L.lane == 0) {
-#pragma unroll
-                        for (int h = 0; h < HP; ++h) {
-                            s_m[slot][h] = st.mref[h];
-                            s_l[slot][h] = lw[h];
-                        }
-                        s_meta[slot][0] = d.b * KC + d.sidx;
-                        s_meta[slot][1] = wr0 + seg_i0;
-                        s_meta[slot][2] = wr0 + i + 1;
-                    }
+                st.store_triple(&s_m[slot][0], &s_l[slot][0], reinterpret_cast<float*>(&s_acc[slot][0][0]), L);
+                if (L.lane == 0) {
+                    // units of this stream's band: [SG pref[b] + band Tb, + Tb)
+                    const int band = d.s / SPW;
+                    const int ubase = SG * s_pref[d.b] + band * d.T;
+                    s_meta[slot][0] = d.b * S + d.s;
+                    s_meta[slot][1] = ubase + seg_lt0;
+                    s_meta[slot][2] = ubase + d.lt + 1;
                 }
             }
         }
@@ -911,13 +874,14 @@ pa_decode_balanced(DecodeArgs a) {
         // The loop runs a multiple of DEPTH tiles and has no exit in its middle (see the
         // fixed route); a padding tile (i >= nk) repeats the last load and is not
         // consumed.
-        uint4 kb[DEPTH][G::UK], vb[DEPTH][G::UV];
-        uint4 qb[DEPTH][G::UK];
+        uint4 kb[DEPTH][G::UK];
+        uint32_t vb[DEPTH][4][G::VW];
+        uint4 qr[DEPTH][G::UK];
         Desc dsc[DEPTH];
 #pragma unroll
         for (int d = 0; d < DEPTH - 1; ++d) {
             if (d > 0 && d < nk) advance();
-            load_tile(min(d, nk - 1), dsc[d], kb[d], vb[d], qb[d]);
+            load_tile(min(d, nk - 1), dsc[d], kb[d], vb[d], qr[d]);
         }
         // The waves of a workgroup have equal work, but a SIMD serves its oldest wave
         // first, so the youngest would finish last with the CU's other waves idle.  A
@@ -939,9 +903,9 @@ pa_decode_balanced(DecodeArgs a) {
                 const int nxt = (d + DEPTH - 1) % DEPTH;
                 const int inext = i + d + DEPTH - 1;
                 if (inext > 0 && inext < nk) advance();
-                load_tile(min(inext, nk - 1), dsc[nxt], kb[nxt], vb[nxt], qb[nxt]);
+                load_tile(min(inext, nk - 1), dsc[nxt], kb[nxt], vb[nxt], qr[nxt]);
                 __builtin_amdgcn_sched_barrier(0);
-                if (DEPTH == 1 || i + d < nk) consume(dsc[d], kb[d], vb[d], qb[d], i + d);
+                if (DEPTH == 1 || i + d < nk) consume(dsc[d], kb[d], vb[d], qr[d], i + d);
                 else __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // see below
             }
         }
@@ -953,9 +917,10 @@ pa_decode_balanced(DecodeArgs a) {
     }
     __syncthreads();
 
-    // Runs of slots: the non-empty slots of one stream are adjacent (slots are in tile
-    // order and a stream's tiles are contiguous).  Wave 0 finds where each run starts;
-    // meanwhile the last wave writes the workgroup's merge descriptor.
+    // Runs of slots: the non-empty slots of one stream are adjacent (waves of one stream
+    // are adjacent, slots are in unit order and a band's units are contiguous).  Wave 0
+    // finds where each run starts; meanwhile the last wave writes the workgroup's merge
+    // record.
     if (wave == 0) {
         const int lane = L.lane;
         const int sid = lane < NS ? s_meta[lane][0] : -1;
@@ -979,41 +944,32 @@ pa_decode_balanced(DecodeArgs a) {
         }
     }
     if (wave == NW - 1 && L.lane == 0) {
-        // The stream holding the last tile, if it starts here and goes on, is merged by
-        // the merge kernel's blocks of this workgroup: {first output row, pieces, the
-        // workspace row of the first piece}.
+        // The band holding the last unit, if it starts here and goes on, is merged by
+        // the merge kernel for this workgroup: {sequence, band, pieces, side of the first
+        // piece}.  The pieces are this workgroup's and one per following workgroup up to
+        // the one holding the band's last unit.
         int4 desc = {0, 0, 0, 0};
         if (g1 > g0) {
-            int b, sidx, lt;
-            locate_tile(g1 - 1, B, KC, s_pref, b, sidx, lt);
+            int b, band, lt;
+            locate_unit(g1 - 1, B, SG, s_pref, b, band, lt);
             const int Tb = s_pref[b + 1] - s_pref[b];
-            const int S = KC * s_pref[b] + sidx * Tb;
-            const int E = S + Tb;
-            if (E > g1 && S >= g0) {
-                // last workgroup the stream reaches: the largest x with split(x) <= E - 1,
-                // i.e. floor((E W - 1) / N) (exact in double, as for split_point)
-                int wl = (int)floor(((double)E * (double)NWG - 1.0) / (double)N);
-                wl = min(wl, NWG - 1);
-                const int kvh = sidx / a.n_chunks;
-                const int chunk = sidx - kvh * a.n_chunks;
-                desc.x = b * a.query_heads + kvh * a.group + chunk * HP;
-                desc.y = wl - w + 1;
-                desc.z = (w * 2 + (S == g0 ? 0 : 1)) * HP;
-            }
+            const int S0 = SG * s_pref[b] + band * Tb;
+            const int E = S0 + Tb;
+            if (E > g1 && S0 >= g0) desc = int4{b, band, wg_of_unit(E - 1, N, NWG) - w + 1, S0 == g0 ? 0 : 1};
         }
         a.ws_desc[w] = desc;
     }
     if (g1 == g0) {
-        // no tiles: an empty triple (weight 0) for a merge whose stream spans this
+        // no units: empty triples (weight 0) for a merge whose band spans this
         // workgroup's (empty) range
-        const size_t wslot = (size_t)w * 2 * HP;
-        for (int idx = tid; idx < HP * C4; idx += NT) {
-            const int h = idx / C4;
-            const int d4 = idx - h * C4;
-            reinterpret_cast<float4_t*>(a.ws_acc + (wslot + h) * D)[d4] = float4_t{0.f, 0.f, 0.f, 0.f};
+        const size_t wslot = (size_t)w * 2 * SPW * HP;
+        for (int idx = tid; idx < SPW * HP * C4; idx += NT) {
+            const int row = idx / C4;
+            const int d4 = idx - row * C4;
+            reinterpret_cast<float4_t*>(a.ws_acc + (wslot + row) * D)[d4] = float4_t{0.f, 0.f, 0.f, 0.f};
             if (d4 == 0) {
-                a.ws_ml[(wslot + h) * 2] = -INFINITY;
-                a.ws_ml[(wslot + h) * 2 + 1] = 0.f;
+                a.ws_ml[(wslot + row) * 2] = -INFINITY;
+                a.ws_ml[(wslot + row) * 2 + 1] = 0.f;
             }
         }
     }
@@ -1021,8 +977,8 @@ pa_decode_balanced(DecodeArgs a) {
 
     // Combine each run: HP * C4 threads per run, as many runs at once as the block holds.
     // A stream covered entirely is finished; otherwise it crosses a workgroup boundary and
-    // its triple goes to the workspace: slot 0 for the stream holding the workgroup's
-    // first tile, slot 1 for the one holding its last tile.
+    // its triple goes to the workspace: side 0 for the band holding the workgroup's first
+    // unit, side 1 for the one holding its last unit.
     constexpr int PER = HP * C4;
     constexpr int RPAR = NT / PER;
     static_assert(RPAR >= 1, "a run needs HP * D / 4 threads");
@@ -1051,89 +1007,177 @@ pa_decode_balanced(DecodeArgs a) {
                     Ls += f * s_l[s][h];
                     o += f * s_acc[s][h][d4];
                 }
-            const int b = sid / KC;
-            const int sidx = sid - b * KC;
+            const int b = sid / S;
+            const int strm = sid - b * S;
+            const int band = strm / SPW;
+            const int spr = strm - band * SPW;
             const int Tb = s_pref[b + 1] - s_pref[b];
-            const int S = KC * s_pref[b] + sidx * Tb;
-            const int kvh = sidx / a.n_chunks;
-            const int chunk = sidx - kvh * a.n_chunks;
+            const int U0 = SG * s_pref[b] + band * Tb;
+            const int kvh = strm / a.n_chunks;
+            const int chunk = strm - kvh * a.n_chunks;
             const size_t row0 = (size_t)b * a.query_heads + kvh * a.group + chunk * HP;
-            if (tb == S && te == S + Tb) {
+            if (tb == U0 && te == U0 + Tb) {
                 reinterpret_cast<float4_t*>(a.out + (row0 + h) * D)[d4] = o / Ls;
             } else {
-                const size_t wslot = ((size_t)w * 2 + (tb == g0 ? 0 : 1)) * HP;
-                reinterpret_cast<float4_t*>(a.ws_acc + (wslot + h) * D)[d4] = o;
+                const size_t wrow = (((size_t)w * 2 + (tb == g0 ? 0 : 1)) * SPW + spr) * HP + h;
+                reinterpret_cast<float4_t*>(a.ws_acc + wrow * D)[d4] = o;
                 if (d4 == 0) {
-                    a.ws_ml[(wslot + h) * 2] = M;
-                    a.ws_ml[(wslot + h) * 2 + 1] = Ls;
+                    a.ws_ml[wrow * 2] = M;
+                    a.ws_ml[wrow * 2 + 1] = Ls;
                 }
             }
         }
     }
+
 }
 
-// Merge of the balanced route: block (w, h) combines head h of the stream that the
-// decode kernel's workgroup w owns (the stream holding w's last tile, when it starts in
-// w and continues past it, so each crossing stream has exactly one owner).  The decode
-// kernel leaves per workgroup a descriptor {first output row, number of pieces, workspace
-// row of the first piece}; the pieces are slot 1 of w (slot 0 if the stream is also w's
-// first) and slot 0 of each following workgroup it reaches, 2 * HP rows apart.
+// Merge of the balanced route.  Workgroup w of the decode kernel owns the band that
+// holds its last unit when that band starts in w and goes on past it (each crossing band
+// has exactly one owner) and leaves a record {sequence, band, pieces n, side of the
+// first piece}; the pieces of stream sp, head h are rows
+// r(0) = ((w * 2 + side) * spw + sp) * HP + h and r(p) = r(0) + p * 2 * spw * HP rows
+// of side 0 of the following workgroups.  Short bands (n <= kShortMerge): block x takes
+// the band of workgroup x, one thread per (row, float4 column), all pieces at once.  Long
+// bands: each of their rows goes to its own block (rows spread round-robin over the
+// grid), whose threads split the pieces in groups and combine them through LDS.
+constexpr int kShortMerge = 16;
+
 template <int D, int HP>
 __global__ void __launch_bounds__(kMergeThreads)
-pa_merge_balanced(DecodeArgs a) {
-    const int w = blockIdx.x / HP;
-    const int h = blockIdx.x - w * HP;
-    const int4 d = a.ws_desc[w];
-    if (d.y <= 0) return;
-    combine_rows<D>(a.ws_ml, a.ws_acc, (size_t)d.z + h, ((size_t)w + 1) * 2 * HP + h, 2 * HP, d.y,
-                    a.out + ((size_t)d.x + h) * D);
+pa_merge_balanced(DecodeArgs a, int n_wg) {
+    constexpr int C4 = D / 4;
+    const int x = blockIdx.x;
+    const int spw = a.spw;
+    const int rows = spw * HP;
+    const size_t stride = (size_t)2 * rows;
+    auto out_row = [&](const int4& d, int row) {
+        const int sp = row / HP;
+        const int h = row - sp * HP;
+        const int s = d.y * spw + sp;
+        const int kvh = s / a.n_chunks;
+        const int chunk = s - kvh * a.n_chunks;
+        return (size_t)d.x * a.query_heads + kvh * a.group + chunk * HP + h;
+    };
+    // short band of workgroup x
+    if (x < n_wg) {
+        const int4 d = a.ws_desc[x];
+        if (d.z > 0 && d.z <= kShortMerge) {
+            for (int idx = threadIdx.x; idx < rows * C4; idx += kMergeThreads) {
+                const int row = idx / C4;
+                const int c = idx - row * C4;
+                const size_t r0 = ((size_t)x * 2 + d.w) * rows + row;
+                float pm[kShortMerge], pl[kShortMerge];
+                float4_t pa[kShortMerge];
+#pragma unroll
+                for (int p = 0; p < kShortMerge; ++p) {
+                    pm[p] = -INFINITY;
+                    pl[p] = 0.f;
+                    pa[p] = float4_t{0.f, 0.f, 0.f, 0.f};
+                    if (p < d.z) {
+                        const size_t r = p == 0 ? r0 : ((size_t)(x + p) * 2) * rows + row;
+                        pa[p] = reinterpret_cast<const float4_t*>(a.ws_acc + r * D)[c];
+                        pm[p] = a.ws_ml[2 * r];
+                        pl[p] = a.ws_ml[2 * r + 1];
+                    }
+                }
+                float M = pm[0];
+#pragma unroll
+                for (int p = 1; p < kShortMerge; ++p) M = fmaxf(M, pm[p]);
+                float Ls = 0.f;
+                float4_t o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int p = 0; p < kShortMerge; ++p) {
+                    const float e = fast_exp2(pm[p] - M);   // 0 for an absent or empty piece
+                    Ls += e * pl[p];
+                    o += e * pa[p];
+                }
+                reinterpret_cast<float4_t*>(a.out + out_row(d, row) * D)[c] = o / Ls;
+            }
+        }
+    }
+    // Rows of long bands: long row k (the row-th row of the j-th long record in workgroup
+    // order, k = j * rows + row) goes to block k % gridDim.x.  The long records are found
+    // with ballots (kMaxBalancedWG records at most, kMergeThreads per round), in order.
+    __shared__ int s_long[kMaxBalancedWG];   // workgroup of the j-th long record
+    __shared__ int s_wcount[kMergeThreads / 64];
+    __shared__ int s_nlong;
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    int base = 0;
+    for (int w0 = 0; w0 < n_wg; w0 += kMergeThreads) {
+        const int w = w0 + threadIdx.x;
+        const bool is_long = w < n_wg && a.ws_desc[w].z > kShortMerge;
+        const uint64_t bal = __builtin_amdgcn_ballot_w64(is_long);
+        const int before = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+        if (lane == 0) s_wcount[wv] = __popcll(bal);
+        __syncthreads();
+        int off = base, total = 0;
+        for (int v = 0; v < kMergeThreads / 64; ++v) {
+            if (v < wv) off += s_wcount[v];
+            total += s_wcount[v];
+        }
+        if (is_long) s_long[off + before] = w;
+        base += total;
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) s_nlong = base;
+    __syncthreads();
+    const int n_long_rows = s_nlong * rows;
+    for (int k = x; k < n_long_rows; k += gridDim.x) {
+        const int w = s_long[k / rows];
+        const int row = k - (k / rows) * rows;
+        const int4 d = a.ws_desc[w];
+        const size_t r0 = ((size_t)w * 2 + d.w) * rows + row;
+        const size_t r1 = ((size_t)w + 1) * 2 * rows + row;
+        combine_rows<D>(a.ws_ml, a.ws_acc, r0, r1, stride, d.z, a.out + out_row(d, row) * D);
+    }
 }
 
 #ifndef PA_WAVES
-#define PA_WAVES 4   // waves per decode workgroup
+#define PA_WAVES 4   // waves per decode workgroup (fixed route)
 #endif
 #ifndef PA_DEPTH
 #define PA_DEPTH 2   // tile buffers per wave (fixed route)
 #endif
-constexpr int kWaves = PA_WAVES;
-constexpr int kDepth = PA_DEPTH;
-
-// Workgroups of a kernel that are resident at once on this device (CUs x blocks per CU),
-// capped at kMaxBalancedWG.  Host-side queries only; nothing is enqueued.
-template <typename K>
-int resident_grid(K kernel, int block, size_t lds) {
-    int dev = 0, cus = 0, per = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, block, lds) != hipSuccess) return 0;
-    const long long g = (long long)cus * (per > 0 ? per : 1);
-    return (int)(g < kMaxBalancedWG ? g : kMaxBalancedWG);
-}
-
-#ifndef PA_BAL_WAVES
-#define PA_BAL_WAVES 12  // waves per balanced workgroup (one workgroup per CU)
-#endif
 #ifndef PA_BAL_DEPTH
 #define PA_BAL_DEPTH 1   // tile buffers per wave (balanced route)
 #endif
-constexpr int kBalWaves = PA_BAL_WAVES;
+constexpr int kWaves = PA_WAVES;
+constexpr int kDepth = PA_DEPTH;
 constexpr int kBalDepth = PA_BAL_DEPTH;
 
-template <int D, int HP, bool SPLIT>
-hipError_t launch_balanced(const Plan& pl, const DecodeArgs& args, hipStream_t stream) {
-    // 12 waves (3 per SIMD) fit the register budget up to 6 heads (4 with pages of 8);
-    // more heads take 8 waves
-    constexpr int NW = (HP <= 4 || (HP <= 6 && !SPLIT)) ? kBalWaves : 8;
+// Compute units of the current device, capped at kMaxBalancedWG.  Host-side queries
+// only; nothing is enqueued.
+int balanced_grid() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    return cus < kMaxBalancedWG ? cus : kMaxBalancedWG;
+}
+
+template <int D, int HP, int NW, bool SPLIT>
+hipError_t launch_balanced_nw(const Plan& pl, const DecodeArgs& args, hipStream_t stream) {
     const auto kern = pa_decode_balanced<D, HP, kBalDepth, NW, SPLIT>;
     const size_t lds = (size_t)(2 * pl.prob.batch + 1) * sizeof(int);
-    const int grid = resident_grid(kern, NW * 64, lds);
+    const int grid = balanced_grid();
     if (grid <= 0) return hipErrorInvalidDevice;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NW * 64), lds, stream, args);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((pa_merge_balanced<D, HP>), dim3((unsigned)(grid * HP)), dim3(kMergeThreads), 0,
-                       stream, args);
+    hipLaunchKernelGGL((pa_merge_balanced<D, HP>), dim3((unsigned)grid), dim3(kMergeThreads), 0, stream, args, grid);
     return hipGetLastError();
+}
+
+template <int D, int HP, bool SPLIT>
+hipError_t launch_balanced(const Plan& pl, const DecodeArgs& args, hipStream_t stream) {
+    switch (pl.bal_waves) {
+        case 12: return launch_balanced_nw<D, HP, 12, SPLIT>(pl, args, stream);
+#ifdef PA_BAL_WAVES
+        case 8: return launch_balanced_nw<D, HP, 8, SPLIT>(pl, args, stream);
+        case 16: return launch_balanced_nw<D, HP, 16, SPLIT>(pl, args, stream);
+#endif
+        default: return hipErrorInvalidValue;
+    }
 }
 
 template <int D, int HP>
@@ -1152,6 +1196,7 @@ hipError_t launch_decode(const Plan& pl, const DecodeArgs& args, hipStream_t str
 
 template <int D>
 hipError_t launch_decode_d(const Plan& pl, const DecodeArgs& args, hipStream_t stream) {
+    static_assert(kMaxHeadsPerWave == 8, "instantiations below cover 1..8 heads");
     switch (pl.heads_per_wg) {
         case 1: return launch_decode<D, 1>(pl, args, stream);
         case 2: return launch_decode<D, 2>(pl, args, stream);
@@ -1201,6 +1246,9 @@ hipError_t launch(const Plan& pl, const void* q, const void* k, const void* v,
     da.n_part_max = pl.n_part_max;
     da.ps_log2 = pl.ps_log2;
     da.force_split = pl.force_split ? 1 : 0;
+    da.spw = pl.spw;
+    da.waves_per_stream = pl.waves_per_stream;
+    da.bands = pl.bands;
 
     hipError_t err = (p.head_dim == 128) ? launch_decode_d<128>(pl, da, stream)
                                          : launch_decode_d<64>(pl, da, stream);
