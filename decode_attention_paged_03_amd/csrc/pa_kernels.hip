@@ -149,13 +149,13 @@ __device__ __forceinline__ void load_q_raw(const _Float16* q, size_t row0, const
 }
 template <int D, int HP>
 __device__ __forceinline__ void fix_q(const uint4 (&qr)[Geo<D>::UK], uint32_t q_sign, const Lane& L,
-                                      half8_t (&qb)[Geo<D>::UK]) {
+                                      uint4 (&qb)[Geo<D>::UK]) {
 #pragma unroll
     for (int j = 0; j < Geo<D>::UK; ++j) {
         uint4 w = qr[j];
         w.x ^= q_sign; w.y ^= q_sign; w.z ^= q_sign; w.w ^= q_sign;
         if (L.n >= HP) w = uint4{0u, 0u, 0u, 0u};
-        qb[j] = as_half8(w);
+        qb[j] = w;
     }
 }
 
@@ -251,12 +251,13 @@ struct WaveState {
     }
 
     // One tile: tokens at or past n_valid are masked (n_valid in 1..16, wave-uniform).
-    __device__ __forceinline__ void tile(const half8_t (&qb)[G::UK], const uint4 (&kb)[G::UK],
+    __device__ __forceinline__ void tile(const uint4 (&qb)[G::UK], const uint4 (&kb)[G::UK],
                                          const uint32_t (&vb)[4][G::VW], int n_valid, float sl2,
                                          const Lane& L) {
         float4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < G::UK; ++j) s = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(kb[j]), qb[j], s, 0, 0, 0);
+        for (int j = 0; j < G::UK; ++j)
+            s = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(kb[j]), as_half8(qb[j]), s, 0, 0, 0);
         // register i: token g + 4 i of head n
         float z[4];
         bool grow = false;
@@ -402,12 +403,9 @@ pa_decode_kernel(DecodeArgs a) {
     const int32_t* bt_row = a.bt + (size_t)b * a.max_pages + pg0;
     for (int i = tid; i < npg; i += NW * 64) s_bt[i] = bt_row[i];
 
-    half8_t qb[G::UK];
-    {
-        uint4 qr[G::UK];
-        load_q_raw<D, HP>(a.q, row0, L, qr);
-        fix_q<D, HP>(qr, a.q_sign, L, qb);
-    }
+    uint4 qb[G::UK];
+    load_q_raw<D, HP>(a.q, row0, L, qb);
+    fix_q<D, HP>(qb, a.q_sign, L, qb);
     __syncthreads();
 
     const size_t tok_bytes = (size_t)a.kv_heads * D * 2;     // bytes between slots
@@ -507,7 +505,7 @@ struct MergeArgs {
     int query_heads, partition, n_part_max, force_split;
 };
 
-constexpr int kMergeThreads = 256;
+constexpr int kMergeThreads = 512;
 
 // Combination of n (max, sum, acc) triples of one output row: out = sum_p e_p acc_p /
 // sum_p e_p l_p with e_p = exp2(m_p - max m).  Triple p is row r(p) of the workspace
@@ -834,7 +832,7 @@ pa_decode_balanced(DecodeArgs a) {
     };
 
     WaveState<D, HP> st;
-    half8_t qb[G::UK];
+    uint4 qb[G::UK];       // B operand of the scores (with one tile buffer, also the load target)
     int seg_lt0 = 0;       // first stream tile of the open segment
     int seg_i0 = 0;        // first wave tile of the open segment
     auto consume = [&](const Desc& d, const uint4 (&kb)[G::UK], const uint32_t (&vb)[4][G::VW],
@@ -876,12 +874,14 @@ pa_decode_balanced(DecodeArgs a) {
         // consumed.
         uint4 kb[DEPTH][G::UK];
         uint32_t vb[DEPTH][4][G::VW];
-        uint4 qr[DEPTH][G::UK];
+        // query rows of a segment's first tile: loaded straight into the operand when there
+        // is one tile buffer (the previous tile is consumed before the next is loaded)
+        uint4 qr[DEPTH > 1 ? DEPTH : 1][G::UK];
         Desc dsc[DEPTH];
 #pragma unroll
         for (int d = 0; d < DEPTH - 1; ++d) {
             if (d > 0 && d < nk) advance();
-            load_tile(min(d, nk - 1), dsc[d], kb[d], vb[d], qr[d]);
+            load_tile(min(d, nk - 1), dsc[d], kb[d], vb[d], qr[d]);   // DEPTH > 1 only
         }
         // The waves of a workgroup have equal work, but a SIMD serves its oldest wave
         // first, so the youngest would finish last with the CU's other waves idle.  A
@@ -903,9 +903,11 @@ pa_decode_balanced(DecodeArgs a) {
                 const int nxt = (d + DEPTH - 1) % DEPTH;
                 const int inext = i + d + DEPTH - 1;
                 if (inext > 0 && inext < nk) advance();
-                load_tile(min(inext, nk - 1), dsc[nxt], kb[nxt], vb[nxt], qr[nxt]);
+                if constexpr (DEPTH == 1) load_tile(min(inext, nk - 1), dsc[nxt], kb[nxt], vb[nxt], qb);
+                else load_tile(min(inext, nk - 1), dsc[nxt], kb[nxt], vb[nxt], qr[nxt]);
                 __builtin_amdgcn_sched_barrier(0);
-                if (DEPTH == 1 || i + d < nk) consume(dsc[d], kb[d], vb[d], qr[d], i + d);
+                if constexpr (DEPTH == 1) consume(dsc[d], kb[d], vb[d], qb, i + d);
+                else if (i + d < nk) consume(dsc[d], kb[d], vb[d], qr[d], i + d);
                 else __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // see below
             }
         }
@@ -1058,42 +1060,62 @@ pa_merge_balanced(DecodeArgs a, int n_wg) {
         const int chunk = s - kvh * a.n_chunks;
         return (size_t)d.x * a.query_heads + kvh * a.group + chunk * HP + h;
     };
+    // All loads that do not depend on a record are issued first: the records' piece
+    // counts (for the long-band scan below) and, speculatively, the first kSpec pieces of
+    // this block's own band for both possible sides of its first piece.
+    constexpr int kScan = kMaxBalancedWG / kMergeThreads;
+    int nz[kScan];
+#pragma unroll
+    for (int q = 0; q < kScan; ++q) {
+        const int w = q * kMergeThreads + threadIdx.x;
+        nz[q] = w < n_wg ? a.ws_desc[w].z : 0;
+    }
+    constexpr int kSpec = 4;
+    const int4 d = x < n_wg ? a.ws_desc[x] : int4{0, 0, 0, 0};
     // short band of workgroup x
-    if (x < n_wg) {
-        const int4 d = a.ws_desc[x];
-        if (d.z > 0 && d.z <= kShortMerge) {
-            for (int idx = threadIdx.x; idx < rows * C4; idx += kMergeThreads) {
-                const int row = idx / C4;
-                const int c = idx - row * C4;
-                const size_t r0 = ((size_t)x * 2 + d.w) * rows + row;
-                float pm[kShortMerge], pl[kShortMerge];
-                float4_t pa[kShortMerge];
+    for (int idx = threadIdx.x; idx < rows * C4; idx += kMergeThreads) {
+        const int row = idx / C4;
+        const int c = idx - row * C4;
+        float pm[kSpec + 1], pl[kSpec + 1];
+        float4_t pa[kSpec + 1];
+        // [0]: first piece on side 1; [p]: piece p on side 0 (p = 0 is the first piece's side 0)
 #pragma unroll
-                for (int p = 0; p < kShortMerge; ++p) {
-                    pm[p] = -INFINITY;
-                    pl[p] = 0.f;
-                    pa[p] = float4_t{0.f, 0.f, 0.f, 0.f};
-                    if (p < d.z) {
-                        const size_t r = p == 0 ? r0 : ((size_t)(x + p) * 2) * rows + row;
-                        pa[p] = reinterpret_cast<const float4_t*>(a.ws_acc + r * D)[c];
-                        pm[p] = a.ws_ml[2 * r];
-                        pl[p] = a.ws_ml[2 * r + 1];
-                    }
-                }
-                float M = pm[0];
-#pragma unroll
-                for (int p = 1; p < kShortMerge; ++p) M = fmaxf(M, pm[p]);
-                float Ls = 0.f;
-                float4_t o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int p = 0; p < kShortMerge; ++p) {
-                    const float e = fast_exp2(pm[p] - M);   // 0 for an absent or empty piece
-                    Ls += e * pl[p];
-                    o += e * pa[p];
-                }
-                reinterpret_cast<float4_t*>(a.out + out_row(d, row) * D)[c] = o / Ls;
-            }
+        for (int p = 0; p <= kSpec; ++p) {
+            const int xw = min(x + (p == kSpec ? 0 : p), n_wg - 1);
+            const size_t r = ((size_t)xw * 2 + (p == kSpec ? 1 : 0)) * rows + row;
+            pa[p] = reinterpret_cast<const float4_t*>(a.ws_acc + r * D)[c];
+            const float2 ml = reinterpret_cast<const float2*>(a.ws_ml)[r];
+            pm[p] = ml.x;
+            pl[p] = ml.y;
         }
+        if (d.z <= 0 || d.z > kShortMerge) continue;
+        if (d.w) {   // the first piece is on side 1
+            pa[0] = pa[kSpec];
+            pm[0] = pm[kSpec];
+            pl[0] = pl[kSpec];
+        }
+        float M = -INFINITY;
+#pragma unroll
+        for (int p = 0; p < kSpec; ++p)
+            if (p < d.z) M = fmaxf(M, pm[p]);
+        // pieces past the speculated ones
+        for (int p = kSpec; p < d.z; ++p) M = fmaxf(M, a.ws_ml[2 * (((size_t)(x + p) * 2) * rows + row)]);
+        float Ls = 0.f;
+        float4_t o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int p = 0; p < kSpec; ++p)
+            if (p < d.z) {
+                const float e = fast_exp2(pm[p] - M);   // 0 for an empty piece
+                Ls += e * pl[p];
+                o += e * pa[p];
+            }
+        for (int p = kSpec; p < d.z; ++p) {
+            const size_t r = ((size_t)(x + p) * 2) * rows + row;
+            const float e = fast_exp2(a.ws_ml[2 * r] - M);
+            Ls += e * a.ws_ml[2 * r + 1];
+            o += e * reinterpret_cast<const float4_t*>(a.ws_acc + r * D)[c];
+        }
+        reinterpret_cast<float4_t*>(a.out + out_row(d, row) * D)[c] = o / Ls;
     }
     // Rows of long bands: long row k (the row-th row of the j-th long record in workgroup
     // order, k = j * rows + row) goes to block k % gridDim.x.  The long records are found
@@ -1104,9 +1126,11 @@ pa_merge_balanced(DecodeArgs a, int n_wg) {
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
     int base = 0;
-    for (int w0 = 0; w0 < n_wg; w0 += kMergeThreads) {
-        const int w = w0 + threadIdx.x;
-        const bool is_long = w < n_wg && a.ws_desc[w].z > kShortMerge;
+#pragma unroll
+    for (int q = 0; q < kScan; ++q) {
+        const int w0 = q * kMergeThreads;
+        if (w0 >= n_wg) break;
+        const bool is_long = nz[q] > kShortMerge;
         const uint64_t bal = __builtin_amdgcn_ballot_w64(is_long);
         const int before = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
         if (lane == 0) s_wcount[wv] = __popcll(bal);
@@ -1116,7 +1140,7 @@ pa_merge_balanced(DecodeArgs a, int n_wg) {
             if (v < wv) off += s_wcount[v];
             total += s_wcount[v];
         }
-        if (is_long) s_long[off + before] = w;
+        if (is_long) s_long[off + before] = w0 + threadIdx.x;
         base += total;
         __syncthreads();
     }
