@@ -80,6 +80,9 @@ constexpr uint32_t kOutOfRange = 0x7FFFFF00u;
 #ifndef PA_XCD_REMAP
 #define PA_XCD_REMAP 1   // balanced route: contiguous work per XCD (see xcd_major)
 #endif
+#ifndef PA_KROW
+#define PA_KROW 1    // balanced route: load K in whole rows and regroup them through LDS
+#endif
 #ifndef PA_BAL_PRIO
 #define PA_BAL_PRIO 1    // balanced route: raise the issue priority of waves that fall behind
 #endif
@@ -188,9 +191,11 @@ __device__ __forceinline__ void buf_ldv(__amdgpu_buffer_rsrc_t r, uint32_t off, 
 // tile's first token; with pages of 8 the tile's tokens 8..15 sit in the next page, whose
 // rows start at `kp2`/`vp2`.  Tokens past n_valid (0..16, wave-uniform) read as zero:
 // their scores are masked, and their zero V rows add nothing.
-//   K: kb[j] = 16 bytes of row ktok, dims 32 j + 8 g .. + 7 (koff = ktok * tok + 16 g).
+//   K: kb[j] = 16 bytes of row ktok, dims 32 j + 8 g .. + 7 (koff = ktok * tok + 16 g);
+//      with KROW (D = 128) K is loaded like V instead: kb[i] = dims 8 n .. 8 n + 7 of row
+//      4 i + g (koff = voff), whole rows per instruction, and regrouped through LDS.
 //   V: vb[i] = dims E n .. E n + E - 1 of row 4 i + g (voff = g * tok + 2 E n).
-template <int D, bool SPLIT>
+template <int D, bool SPLIT, bool KROW = false>
 __device__ __forceinline__ void load_kv(const char* kp, const char* vp, const char* kp2, const char* vp2,
                                         uint32_t koff, uint32_t voff, uint32_t tok_bytes, int n_valid,
                                         const Lane& L, uint4 (&kb)[Geo<D>::UK],
@@ -201,8 +206,13 @@ __device__ __forceinline__ void load_kv(const char* kp, const char* vp, const ch
         const int bytes = n_valid * (int)tok_bytes;
         const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kp, bytes);
         const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vp, bytes);
+        if constexpr (KROW) {
 #pragma unroll
-        for (int j = 0; j < G::UK; ++j) kb[j] = buf_ld128(rk, koff + 64 * j);
+            for (int i = 0; i < 4; ++i) kb[i] = buf_ld128(rk, koff, 4 * i * tok_bytes);
+        } else {
+#pragma unroll
+            for (int j = 0; j < G::UK; ++j) kb[j] = buf_ld128(rk, koff + 64 * j);
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) buf_ldv<G::VW>(rv, voff, 4 * i * tok_bytes, vb[i]);
     } else {
@@ -215,14 +225,23 @@ __device__ __forceinline__ void load_kv(const char* kp, const char* vp, const ch
         // every lane with a wave-uniform resource; the lane's offset into the page it
         // does not use is pushed past the resource's range, so that load returns zero and
         // the two results combine with an OR.
-        const bool first = L.ktok < 8;
-        const uint32_t k1 = first ? koff : kOutOfRange;
-        const uint32_t k2 = first ? kOutOfRange : koff - 8 * tok_bytes;
+        if constexpr (KROW) {
+            // K group i covers rows 4 i .. 4 i + 3, like V
 #pragma unroll
-        for (int j = 0; j < G::UK; ++j) {
-            const uint4 x = buf_ld128(rk1, k1 + 64 * j);
-            const uint4 y = buf_ld128(rk2, k2 + 64 * j);
-            kb[j] = uint4{x.x | y.x, x.y | y.y, x.z | y.z, x.w | y.w};
+            for (int i = 0; i < 4; ++i) {
+                if (i < 2) kb[i] = buf_ld128(rk1, koff, 4 * i * tok_bytes);
+                else kb[i] = buf_ld128(rk2, koff, (4 * i - 8) * tok_bytes);
+            }
+        } else {
+            const bool first = L.ktok < 8;
+            const uint32_t k1 = first ? koff : kOutOfRange;
+            const uint32_t k2 = first ? kOutOfRange : koff - 8 * tok_bytes;
+#pragma unroll
+            for (int j = 0; j < G::UK; ++j) {
+                const uint4 x = buf_ld128(rk1, k1 + 64 * j);
+                const uint4 y = buf_ld128(rk2, k2 + 64 * j);
+                kb[j] = uint4{x.x | y.x, x.y | y.y, x.z | y.z, x.w | y.w};
+            }
         }
         // V group i covers rows 4 i .. 4 i + 3: groups 0, 1 in the first page, 2, 3 in the next
 #pragma unroll
@@ -251,13 +270,33 @@ struct WaveState {
     }
 
     // One tile: tokens at or past n_valid are masked (n_valid in 1..16, wave-uniform).
+    // With KROW, kb holds whole-row K chunks (see load_kv) and kt is this wave's LDS
+    // staging area of 16 slots x 17 16-byte chunks: slot m holds token pi(m) (the row
+    // stride of 17 chunks keeps both the writes and the operand reads free of bank
+    // conflicts); the score operands are read back in the MFMA layout.
+    template <bool KROW = false>
     __device__ __forceinline__ void tile(const uint4 (&qb)[G::UK], const uint4 (&kb)[G::UK],
                                          const uint32_t (&vb)[4][G::VW], int n_valid, float sl2,
-                                         const Lane& L) {
+                                         const Lane& L, uint4* kt = nullptr) {
         float4_t s = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (KROW) {
+            static_assert(D == 128, "whole-row K staging is laid out for 16 chunks per row");
+            // the wave's reads of the previous tile are issued before these writes, and
+            // these writes before the reads below (one wave; LDS executes in order)
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 #pragma unroll
-        for (int j = 0; j < G::UK; ++j)
-            s = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(kb[j]), as_half8(qb[j]), s, 0, 0, 0);
+            for (int i = 0; i < 4; ++i) kt[(4 * L.g + i) * 17 + L.n] = kb[i];   // token 4 i + g = pi(4 g + i)
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+            for (int j = 0; j < G::UK; ++j) {
+                const uint4 kj = kt[L.n * 17 + 4 * j + L.g];
+                s = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(kj), as_half8(qb[j]), s, 0, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < G::UK; ++j)
+                s = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(kb[j]), as_half8(qb[j]), s, 0, 0, 0);
+        }
         // register i: token g + 4 i of head n
         float z[4];
         bool grow = false;
@@ -693,7 +732,7 @@ __device__ __forceinline__ int wg_of_unit(int c, int N, int W) {
     return min(x, W - 1);
 }
 
-template <int D, int HP, int DEPTH, int NW, bool SPLIT>
+template <int D, int HP, int DEPTH, int NW, bool SPLIT, bool KROW>
 __global__ void __launch_bounds__(NW * 64)
 pa_decode_balanced(DecodeArgs a) {
     using G = Geo<D>;
@@ -711,6 +750,7 @@ pa_decode_balanced(DecodeArgs a) {
     __shared__ int s_meta[NS][3];    // stream id (-1: empty), first unit, end unit
     __shared__ int s_runs[NS + 1];   // first slot of each run of one stream's slots, then NS
     __shared__ int s_nruns;
+    __shared__ uint4 s_kt[KROW ? NW * 16 * 17 : 1];   // whole-row K staging, per wave
 
     const int B = a.batch;
     int* s_pref = s_dyn;             // [B + 1]
@@ -746,8 +786,9 @@ pa_decode_balanced(DecodeArgs a) {
     const int ps_log2 = a.ps_log2;
     const size_t tok_bytes = (size_t)a.kv_heads * D * 2;
     const size_t page_bytes = tok_bytes << ps_log2;
-    const uint32_t koff = (uint32_t)(L.ktok * tok_bytes) + 16u * L.g;
     const uint32_t voff = (uint32_t)(L.g * tok_bytes) + 2u * G::E * L.n;
+    const uint32_t koff = KROW ? voff : (uint32_t)(L.ktok * tok_bytes) + 16u * L.g;
+    uint4* const kt = KROW ? &s_kt[wave * 16 * 17] : nullptr;
     const float sl2 = a.scale_log2;
 
     // Physical pages of the wave's units, 64 at a time: lane i holds the page of unit
@@ -826,8 +867,8 @@ pa_decode_balanced(DecodeArgs a) {
         if constexpr (SPLIT) base2 = (size_t)__builtin_amdgcn_readlane(btv2, i & 63) * page_bytes;
         const char* kbase = a.k + (size_t)ckvh * D * 2;
         const char* vbase = a.v + (size_t)ckvh * D * 2;
-        load_kv<D, SPLIT>(kbase + base, vbase + base, kbase + base2, vbase + base2, koff, voff,
-                          (uint32_t)tok_bytes, d.n_valid, L, kb, vb);
+        load_kv<D, SPLIT, KROW>(kbase + base, vbase + base, kbase + base2, vbase + base2, koff, voff,
+                                (uint32_t)tok_bytes, d.n_valid, L, kb, vb);
         if (d.first) load_q_raw<D, HP>(a.q, (size_t)cb * a.query_heads + ckvh * a.group + cchunk * HP, L, qr);
     };
 
@@ -843,7 +884,7 @@ pa_decode_balanced(DecodeArgs a) {
             seg_i0 = i;
             st.reset();
         }
-        st.tile(qb, kb, vb, d.n_valid, sl2, L);
+        st.template tile<KROW>(qb, kb, vb, d.n_valid, sl2, L, kt);
         if (d.lt == d.T - 1 || i == nk - 1) {   // the segment ends here
             const int kvh = d.s / a.n_chunks;
             const int chunk = d.s - kvh * a.n_chunks;
@@ -1181,7 +1222,11 @@ int balanced_grid() {
 
 template <int D, int HP, int NW, bool SPLIT>
 hipError_t launch_balanced_nw(const Plan& pl, const DecodeArgs& args, hipStream_t stream) {
-    const auto kern = pa_decode_balanced<D, HP, kBalDepth, NW, SPLIT>;
+    // Whole-row K loads (staged through LDS): measured faster with up to 4 heads per wave
+    // (serving shape: -1.1 us per call) and slower with 6 (long context: +1.2 us), where
+    // the LDS round trip lengthens each tile more than the wider loads save.
+    constexpr bool krow = PA_KROW && D == 128 && HP <= 4;
+    const auto kern = pa_decode_balanced<D, HP, kBalDepth, NW, SPLIT, krow>;
     const size_t lds = (size_t)(2 * pl.prob.batch + 1) * sizeof(int);
     const int grid = balanced_grid();
     if (grid <= 0) return hipErrorInvalidDevice;
