@@ -83,6 +83,9 @@ constexpr uint32_t kOutOfRange = 0x7FFFFF00u;
 #ifndef PA_KROW
 #define PA_KROW 1    // balanced route: load K in whole rows and regroup them through LDS
 #endif
+#ifndef PA_RUN_SKEW
+#define PA_RUN_SKEW 10   // balanced route: percent by which early rounds of waves get more work
+#endif
 #ifndef PA_BAL_PRIO
 #define PA_BAL_PRIO 1    // balanced route: raise the issue priority of waves that fall behind
 #endif
@@ -763,8 +766,15 @@ pa_decode_balanced(DecodeArgs a) {
     const int RW = a.waves_per_stream;        // waves per stream
     const int SG = a.bands;                   // bands per sequence
     const int S = SG * SPW;                   // streams per sequence
-    const int sp = wave / RW;                 // this wave's stream within a band
-    const int rr = wave - sp * RW;            // this wave's run of the workgroup's range
+    // Waves are handed to the SIMDs in turn (wave i to SIMD i % 4) and a SIMD serves its
+    // older waves first, so the waves of later rounds (i / 4) start later and progress
+    // more slowly.  Runs are therefore assigned round-major -- run rr = wave / SPW, stream
+    // sp = wave % SPW -- and weighted: run rr gets a share proportional to
+    // 1 + skew (RW - 1 - 2 rr) / (RW - 1).  li orders the waves stream-major, so that the
+    // LDS slots of one stream's runs are adjacent.
+    const int rr = wave / SPW;                // this wave's run of the workgroup's range
+    const int sp = wave - rr * SPW;           // this wave's stream within a band
+    const int li = sp * RW + rr;
 
     if (tid < NS) s_meta[tid][0] = -1;
     const int plane = tile_prefix<NT>(a.ctx, B, s_pref, s_ctx, s_wsum);
@@ -779,8 +789,14 @@ pa_decode_balanced(DecodeArgs a) {
     const int w = PA_XCD_REMAP ? xcd_major((int)blockIdx.x, NWG) : (int)blockIdx.x;
     const int g0 = split_point(w, N, NWG);
     const int g1 = split_point(w + 1, N, NWG);
-    const int wr0 = g0 + (int)((long long)(g1 - g0) * rr / RW);
-    const int wr1 = g0 + (int)((long long)(g1 - g0) * (rr + 1) / RW);
+    auto run_start = [&](int r) {   // cumulative weight of runs 0 .. r-1, over the total
+        if (RW == 1) return r == 0 ? g0 : g1;
+        const long long cum = (long long)r * (RW - 1) * (100 + PA_RUN_SKEW) - (long long)PA_RUN_SKEW * r * (r - 1);
+        const long long total = (long long)RW * (RW - 1) * 100;
+        return g0 + (int)((long long)(g1 - g0) * cum / total);
+    };
+    const int wr0 = run_start(rr);
+    const int wr1 = run_start(rr + 1);
     const int nk = wr1 - wr0;
 
     const int ps_log2 = a.ps_log2;
@@ -894,7 +910,7 @@ pa_decode_balanced(DecodeArgs a) {
             } else {
                 // a piece of a stream that continues in another wave: slot 2 wave for the
                 // wave's first segment, 2 wave + 1 for its last one
-                const int slot = 2 * wave + (seg_i0 == 0 ? 0 : 1);
+                const int slot = 2 * li + (seg_i0 == 0 ? 0 : 1);
                 st.store_triple(&s_m[slot][0], &s_l[slot][0], reinterpret_cast<float*>(&s_acc[slot][0][0]), L);
                 if (L.lane == 0) {
                     // units of this stream's band: [SG pref[b] + band Tb, + Tb)
