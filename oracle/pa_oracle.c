@@ -42,6 +42,9 @@
  * with normalised partials).  It exists to pin that combination to the direct
  * definition, in double precision.
  *
+ * pa_oracle_append() is the step before attention in a decode loop: it stores the
+ * new token's key and value rows in the cache (see its own comment).
+ *
  * Error handling: return 0 on success; 1 for a bad argument (sizes, null
  * pointers, query_heads % kv_heads != 0); 2 when a context length or a block
  * table entry that would be dereferenced lies outside the pool.  Nothing is
@@ -260,6 +263,57 @@ int pa_oracle_attend_partitioned(int batch, int query_heads, int kv_heads, int h
     problem_t p = {batch, query_heads, kv_heads, head_dim, page_size, max_pages, num_pages,
                    q, k, v, block_tables, ctx, scale};
     return run(&p, rows, n_rows, partition_size, nthreads, out);
+}
+
+/*
+ * The step before attention: storing the new token's key and value rows.
+ *
+ * The cache exists so that the keys and values of a sequence's earlier tokens are reused
+ * rather than recomputed (the "Paged Attention" section of "[TIL] Optimizing paged
+ * attention"); a decode step therefore first stores its own token's rows.  Under the
+ * layout of that page's "Data Layout" section, the token at position pos of sequence b
+ * belongs in slot pos % page_size of physical page block_tables[b][pos / page_size], so
+ * for every KV head g:
+ *
+ *   K[page][slot][g][:] = new_k[b][g][:]      V[page][slot][g][:] = new_v[b][g][:]
+ *
+ * A negative positions[b] means that sequence stores nothing in this step.  A position
+ * at or past the end of the table row (max_pages * page_size) or a table entry outside
+ * the pool names no slot: that sequence is skipped as well and the cache keeps its old
+ * bytes.  The pages do not describe this step; both rules are this oracle's reading.
+ *
+ * new_k, new_v: fp16 bits [batch][kv_heads][head_dim]; k, v: the caches, modified in
+ * place.  *n_written (may be NULL) receives the number of sequences stored.
+ * Returns 0, or 1 for a bad argument.
+ */
+int pa_oracle_append(int batch, int kv_heads, int head_dim, int page_size, int max_pages,
+                     int num_pages, const uint16_t *new_k, const uint16_t *new_v,
+                     const int32_t *block_tables, const int32_t *positions, uint16_t *k,
+                     uint16_t *v, int *n_written)
+{
+    if (batch < 0 || kv_heads <= 0 || head_dim <= 0 || page_size <= 0 || max_pages <= 0 ||
+        num_pages < 0)
+        return 1;
+    if (batch > 0 && (!new_k || !new_v || !block_tables || !positions || !k || !v)) return 1;
+    int written = 0;
+    for (int b = 0; b < batch; ++b) {
+        long long pos = positions[b];
+        if (pos < 0 || pos >= (long long)max_pages * page_size) continue;
+        long long phys = block_tables[(size_t)b * max_pages + pos / page_size];
+        if (phys < 0 || phys >= num_pages) continue;
+        long long slot = pos % page_size;
+        for (int g = 0; g < kv_heads; ++g) {
+            size_t dst = (size_t)(((phys * page_size + slot) * kv_heads + g) * (long long)head_dim);
+            size_t src = ((size_t)b * kv_heads + g) * (size_t)head_dim;
+            for (int d = 0; d < head_dim; ++d) {
+                k[dst + d] = new_k[src + d];
+                v[dst + d] = new_v[src + d];
+            }
+        }
+        ++written;
+    }
+    if (n_written) *n_written = written;
+    return 0;
 }
 
 /* Threads an OpenMP region would use by default on this machine (1 without OpenMP). */

@@ -39,6 +39,8 @@ def _load(path: Optional[str] = None):
     lib.pa_oracle_attend.restype = I
     lib.pa_oracle_attend_partitioned.argtypes = common + [I, P, I, I, P]
     lib.pa_oracle_attend_partitioned.restype = I
+    lib.pa_oracle_append.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P]
+    lib.pa_oracle_append.restype = I
     lib.pa_oracle_max_threads.argtypes = []
     lib.pa_oracle_max_threads.restype = I
     _libs[path] = lib
@@ -116,3 +118,31 @@ def attend_workload(wl, rows=None, nthreads: int = 1, partition_size: int = 0) -
                                   wl.context_lengths, wl.scale, partition_size, rows, nthreads)
     return attend(wl.query, wl.key_cache, wl.value_cache, wl.block_tables, wl.context_lengths,
                   wl.scale, rows, nthreads)
+
+
+def append(new_key, new_value, block_tables, positions, key_cache, value_cache,
+           lib_path: Optional[str] = None):
+    """Store one new token per sequence: returns (key_cache', value_cache', n_written),
+    copies of the caches with new_key[b] / new_value[b] ([batch][kv_heads][head_dim] fp16)
+    written at position positions[b] of sequence b (skipped when negative or when the
+    position names no slot of the pool).  The input caches are left untouched."""
+    lib = _load(lib_path)
+    k = np.array(key_cache, copy=True, order="C").view(np.uint16)
+    v = np.array(value_cache, copy=True, order="C").view(np.uint16)
+    nk = np.ascontiguousarray(new_key).view(np.uint16)
+    nv = np.ascontiguousarray(new_value).view(np.uint16)
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    pos = np.ascontiguousarray(positions, dtype=np.int32)
+    if k.ndim != 4 or v.shape != k.shape or bt.ndim != 2:
+        raise ValueError("expected K/V [pages][page_size][KVH][D] and bt [B][max_pages]")
+    num_pages, ps, KVH, D = k.shape
+    B = bt.shape[0]
+    if nk.shape != (B, KVH, D) or nv.shape != nk.shape or pos.shape != (B,):
+        raise ValueError("inconsistent shapes")
+    n = ctypes.c_int(0)
+    rc = lib.pa_oracle_append(B, KVH, D, ps, bt.shape[1], num_pages, nk.ctypes.data,
+                              nv.ctypes.data, bt.ctypes.data, pos.ctypes.data, k.ctypes.data,
+                              v.ctypes.data, ctypes.addressof(n))
+    if rc:
+        raise ValueError(f"oracle: {_ERRORS.get(rc, rc)}")
+    return k.view(np.float16), v.view(np.float16), int(n.value)

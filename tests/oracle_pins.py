@@ -52,6 +52,9 @@ class OracleUnderTest:
     def half(self, bits):
         return O.half_to_double(bits, lib_path=self.lib_path)
 
+    def append(self, new_k, new_v, bt, pos, k, v):
+        return O.append(new_k, new_v, bt, pos, k, v, lib_path=self.lib_path)
+
 
 # ----------------------------------------------------------------------------- helpers
 
@@ -321,7 +324,81 @@ def pin_errors_and_empty(ot):
         raise AssertionError(f"no error for {list(over)}")
 
 
+def _append_case(seed, B=5, KVH=3, D=8, ps=4, max_pages=4, num_pages=24):
+    rng = np.random.default_rng(seed)
+    k = rng.standard_normal((num_pages, ps, KVH, D)).astype(np.float16)
+    v = rng.standard_normal((num_pages, ps, KVH, D)).astype(np.float16)
+    owned = rng.permutation(num_pages)[:B * max_pages].reshape(B, max_pages).astype(np.int32)
+    nk = rng.standard_normal((B, KVH, D)).astype(np.float16)
+    nv = rng.standard_normal((B, KVH, D)).astype(np.float16)
+    return k, v, owned, nk, nv
+
+
+def pin_append_numpy_scatter(ot):
+    """Storing a new token equals numpy's own scatter of the rows through the table
+    (fancy-index assignment into the [pages][page_size][KVH][D] view), bit for bit, at
+    positions on page boundaries, inside pages and at the table's last slot; a sequence
+    with a negative position stores nothing."""
+    for seed in range(3):
+        k, v, bt, nk, nv = _append_case(1200 + seed)
+        B, ps, mp = bt.shape[0], k.shape[1], bt.shape[1]
+        pos = np.array([0, ps - 1, ps, mp * ps - 1, -1], dtype=np.int32)[:B]
+        np.random.default_rng(seed).shuffle(pos)
+        k2, v2, n = ot.append(nk, nv, bt, pos, k, v)
+        live = pos >= 0
+        ek, ev = k.copy(), v.copy()
+        ek[bt[live, pos[live] // ps], pos[live] % ps] = nk[live]
+        ev[bt[live, pos[live] // ps], pos[live] % ps] = nv[live]
+        assert n == int(live.sum())
+        assert np.array_equal(k2.view(np.uint16), ek.view(np.uint16)), "key cache"
+        assert np.array_equal(v2.view(np.uint16), ev.view(np.uint16)), "value cache"
+
+
+def pin_append_rebuilds_cache(ot):
+    """Appending every token of a workload one decode step at a time, into a pool that
+    starts as NaN canaries, rebuilds the workload's referenced cache rows exactly; the
+    oracle's attention over the rebuilt cache is then bitwise the one over the original,
+    and every slot no token reaches is still a canary."""
+    wl = tiny(1300, B=3, QH=4, KVH=2, D=8, ps=4, ctx=[1, 9, 16])
+    ps, KVH, D = wl.page_size, wl.kv_heads, wl.head_dim
+    nan = np.full(wl.key_cache.shape, np.nan, dtype=np.float16)
+    k, v = nan.copy(), nan.copy()
+    kf = wl.key_cache.reshape(-1, KVH, D)
+    vf = wl.value_cache.reshape(-1, KVH, D)
+    ctx = wl.context_lengths
+    for t in range(int(ctx.max())):
+        pos = np.where(t < ctx, t, -1).astype(np.int32)
+        rows = np.where(pos >= 0, wl.block_tables[np.arange(wl.batch), np.maximum(pos, 0) // ps]
+                        .astype(np.int64) * ps + np.maximum(pos, 0) % ps, 0)
+        k, v, n = ot.append(kf[rows], vf[rows], wl.block_tables, pos, k, v)
+        assert n == int((pos >= 0).sum())
+    assert np.array_equal(ot.attend(wl, key_cache=k, value_cache=v), ot.attend(wl))
+    touched = np.zeros(wl.key_cache.shape[:2], dtype=bool)
+    for b in range(wl.batch):
+        t = np.arange(int(ctx[b]))
+        touched[wl.block_tables[b, t // ps], t % ps] = True
+    assert np.array_equal(k[touched].view(np.uint16), wl.key_cache[touched].view(np.uint16))
+    assert np.array_equal(v[touched].view(np.uint16), wl.value_cache[touched].view(np.uint16))
+    assert np.isnan(k[~touched]).all() and np.isnan(v[~touched]).all()
+
+
+def pin_append_skips_unaddressable(ot):
+    """A position past the table row or a table entry outside the pool stores nothing:
+    the caches keep every old byte."""
+    k, v, bt, nk, nv = _append_case(1400, B=3)
+    ps, mp, npg = k.shape[1], bt.shape[1], k.shape[0]
+    bad = bt.copy()
+    bad[1, 0] = npg
+    bad[2, 1] = -3
+    pos = np.array([mp * ps, 1, ps + 2], dtype=np.int32)
+    k2, v2, n = ot.append(nk, nv, bad, pos, k, v)
+    assert n == 0
+    assert np.array_equal(k2.view(np.uint16), k.view(np.uint16))
+    assert np.array_equal(v2.view(np.uint16), v.view(np.uint16))
+
+
 ALL_PINS = [pin_half_exhaustive, pin_dense_library, pin_unpaged_identity,
             pin_page_relabel_bitwise, pin_single_token, pin_equal_keys_mean,
             pin_two_token_logistic, pin_hull_and_linearity, pin_large_shift, pin_outlier_keys,
-            pin_partition_identity, pin_canaries_unread, pin_layout_golden, pin_errors_and_empty]
+            pin_partition_identity, pin_canaries_unread, pin_layout_golden, pin_errors_and_empty,
+            pin_append_numpy_scatter, pin_append_rebuilds_cache, pin_append_skips_unaddressable]

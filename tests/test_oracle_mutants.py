@@ -31,6 +31,15 @@ MUTANTS = [
     ("values_from_keys", "const uint16_t *vrow = p->v + kv_offset(p, b, t, g);\n        for (int d = 0; d < p->head_dim; ++d) o[d]",
      "const uint16_t *vrow = p->k + kv_offset(p, b, t, g);\n        for (int d = 0; d < p->head_dim; ++d) o[d]"),
     ("not_normalised", "for (int d = 0; d < p->head_dim; ++d) o[d] /= z;", ""),
+    ("append_slot_from_division", "long long slot = pos % page_size;",
+     "long long slot = pos / page_size % page_size;"),
+    ("append_head_major", "((phys * page_size + slot) * kv_heads + g) * (long long)head_dim",
+     "((phys * kv_heads + g) * page_size + slot) * (long long)head_dim"),
+    ("append_values_from_keys", "v[dst + d] = new_v[src + d];", "v[dst + d] = new_k[src + d];"),
+    ("append_source_transposed", "size_t src = ((size_t)b * kv_heads + g)",
+     "size_t src = ((size_t)g * batch + b)"),
+    ("append_first_sequence_dropped", "for (int b = 0; b < batch; ++b) {\n        long long pos",
+     "for (int b = 1; b < batch; ++b) {\n        long long pos"),
     ("dot_skips_last_dim", "for (int d = 0; d < p->head_dim; ++d)\n        dot +=",
      "for (int d = 0; d + 1 < p->head_dim; ++d)\n        dot +="),
 ]
