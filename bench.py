@@ -50,6 +50,8 @@ def parse():
                     help="tokens per fixed partition (default 0: the library splits the work)")
     ap.add_argument("--rotate-bytes", type=float, default=768e6,
                     help="total K/V bytes to rotate over (cold-cache timing); 0 = one copy")
+    ap.add_argument("--append-steps", type=int, default=200,
+                    help="calls of pa_append timed after the decode steps (0: skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
@@ -65,10 +67,12 @@ def parse():
 
 
 def kernel_source_hash() -> str:
-    """sha256 over the library's sources: counters taken on other sources do not apply."""
+    """sha256 over the sources of the decode kernels and their launch code: counters taken
+    on other sources do not apply.  (pa_append.hip holds a separate kernel, not part of a
+    pa_decode call.)"""
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".cpp", ".h")):
+        if name.endswith((".hip", ".cpp", ".h")) and name != "pa_append.hip":
             with open(os.path.join(CSRC, name), "rb") as f:
                 h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
@@ -113,14 +117,15 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str) -> str:
             per_kernel.setdefault(name, []).append(float(r["Counter_Value"]) * 1024.0 * factor)
         out[counter] = (factor, {k: sum(v) / len(v) for k, v in per_kernel.items()},
                         {k: len(v) for k, v in per_kernel.items()})
-    fetch = sum(out["FETCH_SIZE"][1].values())
-    write = sum(out["WRITE_SIZE"][1].values())
+    # pa_append (timed after the decode steps) is not part of a pa_decode call
+    fetch = sum(v for k, v in out["FETCH_SIZE"][1].items() if not k.startswith("pa_append"))
+    write = sum(v for k, v in out["WRITE_SIZE"][1].items() if not k.startswith("pa_append"))
     lines = [f"# HBM traffic of one pa_decode call, workload {workload}",
              f"kernel_source_sha256: {kernel_source_hash()}",
-             f"command_fetch: rocprofv3 --pmc FETCH_SIZE -d <dir> -- python bench.py --workload {workload} "
-             "--steps 10 --warmup 2 --no-cpu-baseline --copy-calibration",
-             f"command_write: rocprofv3 --pmc WRITE_SIZE -d <dir> -- python bench.py --workload {workload} "
-             "--steps 10 --warmup 2 --no-cpu-baseline --copy-calibration",
+             f"command_fetch: rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o run -- python bench.py --workload {workload} "
+             "--steps 10 --warmup 2 --no-cpu-baseline --copy-calibration --append-steps 0",
+             f"command_write: rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o run -- python bench.py --workload {workload} "
+             "--steps 10 --warmup 2 --no-cpu-baseline --copy-calibration --append-steps 0",
              f"calibration: plain device copy of {COPY_BYTES} B; bytes = counter KiB * 1024 * factor",
              f"fetch_factor: {out['FETCH_SIZE'][0]:.4f}",
              f"write_factor: {out['WRITE_SIZE'][0]:.4f}"]
@@ -156,7 +161,7 @@ def summarize_trace(folder: str, workload: str, steps: int = 200) -> str:
             db.close()
     lines = [f"# rocprofv3 kernel statistics, workload {workload}",
              f"kernel_source_sha256: {kernel_source_hash()}",
-             f"command: rocprofv3 --kernel-trace --stats -d <dir> -o run -- python bench.py "
+             f"command: rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o run -- python bench.py "
              f"--workload {workload} --steps {steps} --no-cpu-baseline",
              "(calls include the warm-up calls; durations in microseconds)",
              f"{'kernel':<48} {'calls':>6} {'avg_us':>9} {'min_us':>9} {'max_us':>9}"]
@@ -165,9 +170,9 @@ def summarize_trace(folder: str, workload: str, steps: int = 200) -> str:
         m = re.search(r"(pa_\w+)(<[^(]*>)?", n)
         short = (m.group(1) + (m.group(2) or "")) if m else n[:48]
         lines.append(f"{short:<48} {c:>6} {a:>9.3f} {lo:>9.3f} {hi:>9.3f}")
-        if m:
+        if m and not m.group(1).startswith("pa_append"):
             per_call += a
-    lines.append(f"sum of pa_* kernel averages (one call): {per_call:.3f} us")
+    lines.append(f"sum of the decode kernels' averages (one pa_decode call): {per_call:.3f} us")
     path = os.path.join(PROFILES, f"kernels_{workload}.txt")
     os.makedirs(PROFILES, exist_ok=True)
     with open(path, "w") as f:
@@ -236,6 +241,65 @@ def cpu_baseline(wl, target_s: float):
                       f"{cores} OpenMP threads"}
 
 
+def measure_append(dec, wl, k, v, bt, stream, steps: int):
+    """Time pa_append, the step that stores each sequence's new key/value rows before the
+    decode: every sequence rewrites the slot of its newest cached token with the bytes
+    already there, so the caches (and later decodes) are unchanged.  Bytes per call: the
+    new rows read and written (K and V), plus one position and one table entry per
+    sequence."""
+    import numpy as np
+    import torch
+    if steps <= 0:
+        return None
+    ps = wl.page_size
+    last = wl.context_lengths.astype(np.int64) - 1
+    live = last >= 0
+    page = torch.from_numpy(np.where(live, wl.block_tables[np.arange(wl.batch),
+                                                           np.maximum(last, 0) // ps], 0)
+                            .astype(np.int64)).to(k.device)
+    slot = torch.from_numpy(np.maximum(last, 0) % ps).to(k.device)
+    new_k = k[page, slot].contiguous()
+    new_v = v[page, slot].contiguous()
+    pos = torch.from_numpy(np.where(live, last, -1).astype(np.int32)).to(k.device)
+    for _ in range(5):
+        dec.append(new_k, new_v, k, v, bt, pos, stream=stream)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    # eager: each call also pays the Python binding's enqueue cost, which is longer than
+    # the kernel, so back-to-back calls measure the host
+    start.record(stream)
+    for _ in range(steps):
+        dec.append(new_k, new_v, k, v, bt, pos, stream=stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    us_eager = start.elapsed_time(end) / steps * 1e3
+    # the same calls recorded once into a HIP graph and replayed: device time per call
+    reps = 20
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(reps):
+            dec.append(new_k, new_v, k, v, bt, pos)
+    graph.replay()
+    torch.cuda.synchronize()
+    n_replay = max(1, steps // reps)
+    cur = torch.cuda.current_stream()
+    start.record(cur)
+    for _ in range(n_replay):
+        graph.replay()
+    end.record(cur)
+    torch.cuda.synchronize()
+    us = start.elapsed_time(end) / (n_replay * reps) * 1e3
+    n = int(live.sum())
+    nbytes = 2 * 2 * n * wl.kv_heads * wl.head_dim * 2 + 2 * 4 * wl.batch
+    return {"kernel": "pa_append_kernel", "us_per_call": round(us, 3),
+            "us_per_call_eager": round(us_eager, 3),
+            "bytes_per_call": nbytes, "GB/s": round(nbytes / (us * 1e-6) / 1e9, 3),
+            "frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 6),
+            "timing": f"HIP events around {n_replay} replays of a graph of {reps} calls "
+                      f"(eager: {steps} back-to-back calls)"}
+
+
 def main():
     args = parse()
     if args.summarize_trace:
@@ -302,6 +366,8 @@ def main():
     avg_launch_ms = region_ms / args.steps
     achieved = kv_bytes / (avg_launch_ms * 1e-3) / 1e9
 
+    append_line = measure_append(dec, wl, ks[0], vs[0], bt, stream, args.append_steps)
+
     if args.copy_calibration:
         n = COPY_BYTES // 4
         src = torch.randn(n, device=dev)
@@ -354,6 +420,8 @@ def main():
             "timing": f"HIP events on the call's stream around {args.steps} back-to-back calls",
         },
     }
+    if append_line:
+        line["append"] = append_line
     dec.close()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)

@@ -168,6 +168,29 @@ pa_status pa_decode(const pa_handle* handle, const void* query, const void* key_
     return err == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
+pa_status pa_append(const pa_handle* handle, const void* new_key, const void* new_value,
+                    void* key_cache, void* value_cache, const int32_t* block_tables,
+                    const int32_t* positions, hipStream_t stream) {
+    if (!handle || !new_key || !new_value || !key_cache || !value_cache || !block_tables ||
+        !positions)
+        return PA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(new_key) || !aligned16(new_value) || !aligned16(key_cache) ||
+        !aligned16(value_cache))
+        return PA_ERR_MISALIGNED;
+    const pa::Plan& pl = handle->plan;
+    // grid: one workgroup column per sequence (x), the sequence's row chunks along y
+    const long long row_chunks = (long long)pl.prob.kv_heads * (pl.prob.head_dim / 8);
+    const long long threads = pa::append_threads(row_chunks);
+    // a page's bytes address one buffer resource (32-bit range)
+    if (row_chunks * 16 * pl.prob.page_size > INT32_MAX ||
+        (row_chunks + threads - 1) / threads > 65535 ||
+        (long long)pl.prob.batch * threads > UINT32_MAX)
+        return PA_ERR_UNSUPPORTED;
+    hipError_t err = pa::launch_append(pl, new_key, new_value, key_cache, value_cache,
+                                       block_tables, positions, stream);
+    return err == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
 pa_status pa_destroy(pa_handle* handle) {
     delete handle;
     return PA_OK;

@@ -57,4 +57,16 @@ hipError_t launch(const Plan& plan, const void* q, const void* k, const void* v,
                   const int32_t* block_tables, const int32_t* ctx, float scale, float* out,
                   void* workspace, hipStream_t stream);
 
+// pa_append: workgroup size for a sequence's kv_heads * head_dim / 8 16-byte chunks (whole
+// waves, at most kAppendThreads; more chunks take more workgroups along grid y).
+constexpr int kAppendThreads = 256;
+inline int append_threads(long long row_chunks) {
+    return row_chunks >= kAppendThreads ? kAppendThreads : (int)((row_chunks + 63) / 64 * 64);
+}
+
+// Enqueue the kernel that stores one new key / value row per sequence (pa_append).
+hipError_t launch_append(const Plan& plan, const void* new_k, const void* new_v, void* k_cache,
+                         void* v_cache, const int32_t* block_tables, const int32_t* positions,
+                         hipStream_t stream);
+
 }  // namespace pa

@@ -1,7 +1,7 @@
 """ctypes binding of libpa.so -- argument marshalling only.
 
 The functions below carry the C ABI's names (``pa_create``, ``pa_workspace_size``,
-``pa_decode``, ``pa_destroy``, ``pa_status_string``) and take plain integers for
+``pa_decode``, ``pa_append``, ``pa_destroy``, ``pa_status_string``) and take plain integers for
 device pointers and the stream.  ``PagedDecoder`` is a convenience wrapper that
 takes torch tensors, checks their dtype / device / contiguity and passes their
 ``data_ptr()`` through; every step of the computation runs in the library's HIP
@@ -27,7 +27,8 @@ PA_ERR_NO_MEMORY = 6
 PA_FLAG_FORCE_SPLIT = 0x1
 PA_FLAG_FORCE_SINGLE = 0x2
 
-EXPORTED = ("pa_create", "pa_workspace_size", "pa_decode", "pa_destroy", "pa_status_string")
+EXPORTED = ("pa_create", "pa_workspace_size", "pa_decode", "pa_append", "pa_destroy",
+            "pa_status_string")
 
 
 class pa_problem(ctypes.Structure):
@@ -63,6 +64,8 @@ def load() -> ctypes.CDLL:
     lib.pa_workspace_size.restype = ctypes.c_int
     lib.pa_decode.argtypes = [P, P, P, P, P, P, ctypes.c_float, P, P, ctypes.c_size_t, P]
     lib.pa_decode.restype = ctypes.c_int
+    lib.pa_append.argtypes = [P, P, P, P, P, P, P, P]
+    lib.pa_append.restype = ctypes.c_int
     lib.pa_destroy.argtypes = [P]
     lib.pa_destroy.restype = ctypes.c_int
     lib.pa_status_string.argtypes = [ctypes.c_int]
@@ -98,6 +101,14 @@ def pa_decode(handle, query: int, key_cache: int, value_cache: int, block_tables
                           float(scale), out, workspace or None, int(workspace_bytes), stream or None)
     if st != PA_OK:
         raise PaError(st, "pa_decode")
+
+
+def pa_append(handle, new_key: int, new_value: int, key_cache: int, value_cache: int,
+              block_tables: int, positions: int, stream: int) -> None:
+    st = load().pa_append(handle, new_key, new_value, key_cache, value_cache, block_tables,
+                          positions, stream or None)
+    if st != PA_OK:
+        raise PaError(st, "pa_append")
 
 
 def pa_destroy(handle) -> None:
@@ -155,6 +166,36 @@ class PagedDecoder:
                   block_tables.data_ptr(), context_lengths.data_ptr(), scale, out.data_ptr(),
                   ws.data_ptr() if ws is not None else 0, self.workspace_bytes, stream.cuda_stream)
         return out
+
+    def append(self, new_key, new_value, key_cache, value_cache, block_tables, positions,
+               stream=None):
+        """Store new_key[b] / new_value[b] ([batch][kv_heads][head_dim] fp16) at position
+        positions[b] of sequence b, in place in key_cache / value_cache."""
+        import torch
+        p = self.problem
+        for name, t, dt in (("new_key", new_key, torch.float16),
+                            ("new_value", new_value, torch.float16),
+                            ("key_cache", key_cache, torch.float16),
+                            ("value_cache", value_cache, torch.float16),
+                            ("block_tables", block_tables, torch.int32),
+                            ("positions", positions, torch.int32)):
+            if t.dtype != dt or not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"{name}: need a contiguous {dt} CUDA tensor")
+        if tuple(new_key.shape) != (p.batch, p.kv_heads, p.head_dim) or \
+                new_value.shape != new_key.shape:
+            raise ValueError("new key/value shape")
+        if tuple(key_cache.shape) != (p.num_physical_pages, p.page_size, p.kv_heads, p.head_dim) \
+                or key_cache.shape != value_cache.shape:
+            raise ValueError("key/value cache shape")
+        if tuple(block_tables.shape) != (p.batch, p.max_pages_per_sequence):
+            raise ValueError("block table shape")
+        if tuple(positions.shape) != (p.batch,):
+            raise ValueError("positions shape")
+        if stream is None:
+            stream = torch.cuda.current_stream(new_key.device)
+        pa_append(self.handle, new_key.data_ptr(), new_value.data_ptr(), key_cache.data_ptr(),
+                  value_cache.data_ptr(), block_tables.data_ptr(), positions.data_ptr(),
+                  stream.cuda_stream)
 
     def close(self):
         if self.handle:

@@ -73,7 +73,8 @@ typedef struct pa_problem {
     int32_t head_dim;               /* 64 or 128                                                  */
     int32_t page_size;              /* tokens per page: power of two, 8 .. 256                    */
     int32_t max_pages_per_sequence; /* row stride of block_tables                                 */
-    int32_t num_physical_pages;     /* pages in each of key_cache / value_cache (informational)   */
+    int32_t num_physical_pages;     /* pages in each of key_cache / value_cache (pa_append writes
+                                       only below it)                                             */
     int32_t partition_size;         /* tokens per partition, multiple of page_size, at most
                                        512 pages; 0 -> the library's default                      */
     int32_t max_context_length;     /* bound on every context_lengths[b]; sizes the grid and the
@@ -110,6 +111,28 @@ pa_status pa_decode(const pa_handle *handle, const void *query, const void *key_
                     const void *value_cache, const int32_t *block_tables,
                     const int32_t *context_lengths, float scale, float *out, void *workspace,
                     size_t workspace_bytes, hipStream_t stream);
+
+/* Enqueue the step before a decode: store one new token's key and value rows per
+ * sequence in the paged cache.  The cache exists so that earlier tokens' keys and values
+ * are reused rather than recomputed ("Paged Attention" section of the page named above);
+ * under its "Data Layout" section the token at position pos of sequence b belongs in slot
+ * pos % page_size of physical page block_tables[b][pos / page_size].
+ *   new_key, new_value  fp16 [batch][kv_heads][head_dim], 16-byte aligned
+ *   key_cache, value_cache  the caches pa_decode() reads (same layout), 16-byte aligned;
+ *                   written in place, one row per (sequence, KV head)
+ *   block_tables    int32 [batch][max_pages_per_sequence]
+ *   positions       int32 [batch]: the new token's position (the context length before
+ *                   the step); a negative position stores nothing for that sequence
+ * A position at or past max_pages_per_sequence * page_size, or a table entry outside
+ * [0, num_physical_pages), names no slot: that sequence is skipped and no byte outside the
+ * pool is written.  Two sequences must not name the same slot (the stores would race).
+ * Uses the batch, kv_heads, head_dim, page_size, max_pages_per_sequence and
+ * num_physical_pages of the handle's problem; needs no workspace; allocates nothing and
+ * does not synchronise.  A following pa_decode() on the same stream with
+ * context_lengths[b] = positions[b] + 1 attends over the new token. */
+pa_status pa_append(const pa_handle *handle, const void *new_key, const void *new_value,
+                    void *key_cache, void *value_cache, const int32_t *block_tables,
+                    const int32_t *positions, hipStream_t stream);
 
 /* Free the handle; NULL is accepted. */
 pa_status pa_destroy(pa_handle *handle);

@@ -143,6 +143,25 @@ def test_decode_rejects_before_any_hip_call(lib):
         pa.pa_destroy(h)
 
 
+def test_append_rejects_before_any_hip_call(lib):
+    h = pa.pa_create(good())
+    A = 0x10000          # aligned fake device addresses: never dereferenced on these paths
+    try:
+        names = ("new_key", "new_value", "key_cache", "value_cache", "block_tables", "positions")
+
+        def status(**over):
+            a = dict.fromkeys(names, A)
+            a.update(over)
+            return lib.pa_append(h, *(a[n] for n in names), None)
+        for name in names:
+            assert status(**{name: None}) == pa.PA_ERR_INVALID_ARGUMENT, name
+        for name in ("new_key", "new_value", "key_cache", "value_cache"):
+            assert status(**{name: A + 8}) == pa.PA_ERR_MISALIGNED, name
+        assert lib.pa_append(None, A, A, A, A, A, A, None) == pa.PA_ERR_INVALID_ARGUMENT
+    finally:
+        pa.pa_destroy(h)
+
+
 def test_status_strings(lib):
     names = ["PA_OK", "PA_ERR_INVALID_ARGUMENT", "PA_ERR_UNSUPPORTED", "PA_ERR_MISALIGNED",
              "PA_ERR_WORKSPACE", "PA_ERR_HIP", "PA_ERR_NO_MEMORY"]
