@@ -92,6 +92,9 @@ int build_plan(const pa_problem* in, Plan* pl) {
     long long nparts = ((long long)p.max_context_length + partition - 1) / partition;
     out.n_part_max = (int)(nparts < 1 ? 1 : nparts);
     out.force_split = (p.flags & PA_FLAG_FORCE_SPLIT) != 0;
+    // the merge reads one output row's partition triples through a buffer resource with a
+    // 32-bit range
+    if (!out.balanced && (long long)out.n_part_max * p.head_dim * 4 > INT32_MAX) return PA_ERR_UNSUPPORTED;
 
     const long long grid = (long long)p.batch * p.kv_heads * out.n_chunks * out.n_part_max;
     const long long mgrid = (long long)p.batch * p.query_heads;
@@ -106,12 +109,12 @@ int build_plan(const pa_problem* in, Plan* pl) {
         out.bands = streams / out.spw;
         // Rows of D floats (plus a (max, sum) pair each): per workgroup (up to
         // kMaxBalancedWG), two sides x spw streams x heads_per_wg heads of piece
-        // triples; then one 16-byte merge record per workgroup.
+        // triples; then two 16-byte merge records per workgroup.
         out.need_merge = true;
         const size_t rows = (size_t)kMaxBalancedWG * 2 * out.spw * out.heads_per_wg;
         out.ws_ml_offset = rows * (size_t)p.head_dim * sizeof(float);
         out.ws_desc_offset = out.ws_ml_offset + rows * 2 * sizeof(float);
-        out.ws_bytes = out.ws_desc_offset + (size_t)kMaxBalancedWG * 16;
+        out.ws_bytes = out.ws_desc_offset + (size_t)kMaxBalancedWG * 2 * 16;
     } else {
         out.need_merge = out.force_split || out.n_part_max > 1;
         if (out.need_merge) {

@@ -548,14 +548,22 @@ struct MergeArgs {
 };
 
 constexpr int kMergeThreads = 512;
+// Balanced route: a band whose pieces span at most this many workgroups is merged by the
+// block of the workgroup where it starts, all pieces at once; longer bands have their
+// rows dealt out over the blocks of the workgroups they span.
+constexpr int kShortMerge = 16;
 
 // Combination of n (max, sum, acc) triples of one output row: out = sum_p e_p acc_p /
 // sum_p e_p l_p with e_p = exp2(m_p - max m).  Triple p is row r(p) of the workspace
 // (max, sum at ws_ml[2 r], acc at ws_acc[D r]) with r(0) = row_first and
-// r(p) = row_rest + (p - 1) * stride.  One pass: thread (g, c) folds the triples
-// p = g, g + GR, ... for float4 column c into a running triple, rescaling whenever its
-// maximum grows; the GR partial triples are then combined through LDS.  Every thread of
-// the block takes part.  At least one triple has a finite maximum.
+// r(p) = row_rest + (p - 1) * stride.  One pass: thread (g, c) folds triple 0 (group 0)
+// and the triples p = 1 + g, 1 + g + GR, ... for float4 column c into a running triple,
+// rescaling whenever its maximum grows; the GR partial triples are then combined through
+// LDS.  Triples past the first are read with buffer loads over exactly their rows: the
+// lane's part of the offset stays in one register and the part shared by the wave
+// (which triple of the group) is a scalar operand, so a batch of UNR loads in flight
+// costs no address registers.  Every thread of the block takes part.  At least one
+// triple has a finite maximum.
 template <int D>
 __device__ __forceinline__ void combine_rows(const float* ws_ml, const float* ws_acc, size_t row_first,
                                              size_t row_rest, size_t stride, int n, float* out_row) {
@@ -570,35 +578,55 @@ __device__ __forceinline__ void combine_rows(const float* ws_ml, const float* ws
     const int g = tid / C4;
     float m = -INFINITY, l = 0.f;
     float4_t o = {0.f, 0.f, 0.f, 0.f};
-    for (int p0 = g; p0 < n; p0 += GR * UNR) {
-        float4_t av[UNR];
-        float2 mv[UNR];
-#pragma unroll
-        for (int k = 0; k < UNR; ++k) {
-            const int p = p0 + k * GR;
-            if (p < n) {
-                const size_t r = p == 0 ? row_first : row_rest + (size_t)(p - 1) * stride;
-                av[k] = reinterpret_cast<const float4_t*>(ws_acc + r * D)[c];
-                mv[k] = reinterpret_cast<const float2*>(ws_ml)[r];
-            } else {
-                av[k] = float4_t{0.f, 0.f, 0.f, 0.f};
-                mv[k] = make_float2(-INFINITY, 0.f);
-            }
-        }
-        float mb = m;
-#pragma unroll
-        for (int k = 0; k < UNR; ++k) mb = fmaxf(mb, mv[k].x);
-        if (mb != -INFINITY) {
-            const float a0 = fast_exp2(m - mb);     // 0 while nothing was folded in yet
-            l *= a0;
-            o *= a0;
+    if (g == 0) {   // triple 0
+        o = reinterpret_cast<const float4_t*>(ws_acc + row_first * D)[c];
+        const float2 ml = reinterpret_cast<const float2*>(ws_ml)[row_first];
+        m = ml.x;
+        l = ml.y;
+    }
+    const int nr = n - 1;                           // triples at row_rest + q * stride
+    if (nr > 0) {
+        const uint32_t acc_row = (uint32_t)(stride * D * 4);   // bytes between triples
+        const uint32_t ml_row = (uint32_t)(stride * 8);
+        const __amdgpu_buffer_rsrc_t racc =
+            tile_rsrc(reinterpret_cast<const char*>(ws_acc + row_rest * D), (int)(nr * acc_row));
+        const __amdgpu_buffer_rsrc_t rml =
+            tile_rsrc(reinterpret_cast<const char*>(ws_ml + row_rest * 2), (int)(nr * ml_row));
+        const uint32_t vacc = (uint32_t)g * acc_row + 16u * c;
+        const uint32_t vml = (uint32_t)g * ml_row;
+        typedef float f32x2_t __attribute__((ext_vector_type(2)));
+        for (int q0 = 0; q0 < nr; q0 += GR * UNR) {
+            float4_t av[UNR];
+            float2 mv[UNR];
 #pragma unroll
             for (int k = 0; k < UNR; ++k) {
-                const float e = fast_exp2(mv[k].x - mb);
-                l += e * mv[k].y;
-                o += e * av[k];
+                const uint32_t qs = (uint32_t)(q0 + k * GR);   // wave-uniform
+                // (scalar offsets are wave-uniform; readfirstlane keeps the compiler from
+                // carrying them in vector registers, which costs a loop per load)
+                const int sacc = __builtin_amdgcn_readfirstlane((int)(qs * acc_row));
+                const int sml = __builtin_amdgcn_readfirstlane((int)(qs * ml_row));
+                av[k] = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(racc, (int)vacc, sacc, 0));
+                // (the whole vector is reinterpreted: bit-casting single elements of the
+                // load's result made clang read one dword for both)
+                const f32x2_t t = __builtin_bit_cast(f32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rml, (int)vml, sml, 0));
+                const bool live = q0 + k * GR + g < nr;
+                mv[k] = make_float2(live ? t.x : -INFINITY, t.y);
             }
-            m = mb;
+            float mb = m;
+#pragma unroll
+            for (int k = 0; k < UNR; ++k) mb = fmaxf(mb, mv[k].x);
+            if (mb != -INFINITY) {
+                const float a0 = fast_exp2(m - mb);     // 0 while nothing was folded in yet
+                l *= a0;
+                o *= a0;
+#pragma unroll
+                for (int k = 0; k < UNR; ++k) {
+                    const float e = fast_exp2(mv[k].x - mb);   // 0 for a triple past the end
+                    l += e * mv[k].y;
+                    o += e * av[k];
+                }
+                m = mb;
+            }
         }
     }
     if (c == 0) {
@@ -1003,20 +1031,36 @@ pa_decode_balanced(DecodeArgs a) {
         }
     }
     if (wave == NW - 1 && L.lane == 0) {
-        // The band holding the last unit, if it starts here and goes on, is merged by
-        // the merge kernel for this workgroup: {sequence, band, pieces, side of the first
-        // piece}.  The pieces are this workgroup's and one per following workgroup up to
-        // the one holding the band's last unit.
-        int4 desc = {0, 0, 0, 0};
+        // The workgroup's two merge records.  [0]: the band holding its last unit, if it
+        // starts here and goes on -- {sequence, band, pieces n, side of the first piece};
+        // the pieces are this workgroup's and one per following workgroup up to the one
+        // holding the band's last unit.  [1]: the band holding its first unit, if that
+        // band started in an earlier workgroup o and is long (n > kShortMerge): this
+        // workgroup's merge block then combines some of its rows -- {sequence, band,
+        // 2 o + side of o's piece, n}; n = 0 otherwise.
+        int4 own = {0, 0, 0, 0};
+        int4 cov = {0, 0, 0, 0};
         if (g1 > g0) {
             int b, band, lt;
             locate_unit(g1 - 1, B, SG, s_pref, b, band, lt);
             const int Tb = s_pref[b + 1] - s_pref[b];
             const int S0 = SG * s_pref[b] + band * Tb;
             const int E = S0 + Tb;
-            if (E > g1 && S0 >= g0) desc = int4{b, band, wg_of_unit(E - 1, N, NWG) - w + 1, S0 == g0 ? 0 : 1};
+            if (E > g1 && S0 >= g0) own = int4{b, band, wg_of_unit(E - 1, N, NWG) - w + 1, S0 == g0 ? 0 : 1};
         }
-        a.ws_desc[w] = desc;
+        if (g0 < N) {
+            int b, band, lt;
+            locate_unit(g0, B, SG, s_pref, b, band, lt);
+            const int Tb = s_pref[b + 1] - s_pref[b];
+            const int S0 = SG * s_pref[b] + band * Tb;
+            if (S0 < g0) {
+                const int o = wg_of_unit(S0, N, NWG);
+                const int n = wg_of_unit(S0 + Tb - 1, N, NWG) - o + 1;
+                if (n > kShortMerge) cov = int4{b, band, 2 * o + (S0 == split_point(o, N, NWG) ? 0 : 1), n};
+            }
+        }
+        a.ws_desc[2 * w] = own;
+        a.ws_desc[2 * w + 1] = cov;
     }
     if (g1 == g0) {
         // no units: empty triples (weight 0) for a merge whose band spans this
@@ -1092,15 +1136,15 @@ pa_decode_balanced(DecodeArgs a) {
 
 // Merge of the balanced route.  Workgroup w of the decode kernel owns the band that
 // holds its last unit when that band starts in w and goes on past it (each crossing band
-// has exactly one owner) and leaves a record {sequence, band, pieces n, side of the
-// first piece}; the pieces of stream sp, head h are rows
+// has exactly one owner); the pieces of stream sp, head h of such a band are rows
 // r(0) = ((w * 2 + side) * spw + sp) * HP + h and r(p) = r(0) + p * 2 * spw * HP rows
-// of side 0 of the following workgroups.  Short bands (n <= kShortMerge): block x takes
-// the band of workgroup x, one thread per (row, float4 column), all pieces at once.  Long
-// bands: each of their rows goes to its own block (rows spread round-robin over the
-// grid), whose threads split the pieces in groups and combine them through LDS.
-constexpr int kShortMerge = 16;
-
+// of side 0 of the following workgroups.  Merge block x reads workgroup x's two records
+// (written by the decode kernel, no search here):
+//   * a short band it owns (n <= kShortMerge): one thread per (row, float4 column), all
+//     pieces at once;
+//   * rows of long bands: the n blocks of the workgroups a long band spans take rows
+//     j, j + n, ... (j = x - owner), each row with all threads of the block, so the
+//     rows of one long band are spread over the machine.
 template <int D, int HP>
 __global__ void __launch_bounds__(kMergeThreads)
 pa_merge_balanced(DecodeArgs a, int n_wg) {
@@ -1109,108 +1153,95 @@ pa_merge_balanced(DecodeArgs a, int n_wg) {
     const int spw = a.spw;
     const int rows = spw * HP;
     const size_t stride = (size_t)2 * rows;
-    auto out_row = [&](const int4& d, int row) {
+    auto out_row = [&](int b, int band, int row) {
         const int sp = row / HP;
         const int h = row - sp * HP;
-        const int s = d.y * spw + sp;
+        const int s = band * spw + sp;
         const int kvh = s / a.n_chunks;
         const int chunk = s - kvh * a.n_chunks;
-        return (size_t)d.x * a.query_heads + kvh * a.group + chunk * HP + h;
+        return (size_t)b * a.query_heads + kvh * a.group + chunk * HP + h;
     };
-    // All loads that do not depend on a record are issued first: the records' piece
-    // counts (for the long-band scan below) and, speculatively, the first kSpec pieces of
-    // this block's own band for both possible sides of its first piece.
-    constexpr int kScan = kMaxBalancedWG / kMergeThreads;
-    int nz[kScan];
-#pragma unroll
-    for (int q = 0; q < kScan; ++q) {
-        const int w = q * kMergeThreads + threadIdx.x;
-        nz[q] = w < n_wg ? a.ws_desc[w].z : 0;
-    }
-    constexpr int kSpec = 4;
-    const int4 d = x < n_wg ? a.ws_desc[x] : int4{0, 0, 0, 0};
-    // short band of workgroup x
+    constexpr int kFirstPieces = 4;   // pieces loaded for every short band (more if needed)
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    // Pieces of a band owned by workgroup x, relative to its first row (x * 2) * rows:
+    // piece 0 at side * rows rows, piece p >= 1 at p * 2 * rows rows (side 0 of workgroup
+    // x + p).  One buffer resource spans them; the lane's (row, column) part of an offset
+    // is a register, the piece's part a scalar.
+    const uint32_t acc_row = (uint32_t)(D * 4);
+    const uint32_t acc_wg = (uint32_t)(2 * rows) * acc_row;        // bytes per workgroup
+    const uint32_t ml_wg = (uint32_t)(2 * rows) * 8u;
+    const char* acc_base = reinterpret_cast<const char*>(a.ws_acc) + (size_t)x * acc_wg;
+    const char* ml_base = reinterpret_cast<const char*>(a.ws_ml) + (size_t)x * ml_wg;
+    const int span = min(kShortMerge, n_wg - x);                    // workgroups x .. x + span - 1
+    const __amdgpu_buffer_rsrc_t racc0 = tile_rsrc(acc_base, (int)(span * acc_wg));
+    const __amdgpu_buffer_rsrc_t rml0 = tile_rsrc(ml_base, (int)(span * ml_wg));
+    auto piece_off = [&](int p, int side, uint32_t per_wg, uint32_t per_row) {   // wave-uniform
+        return __builtin_amdgcn_readfirstlane((int)(p == 0 ? (uint32_t)side * (uint32_t)rows * per_row : (uint32_t)p * per_wg));
+    };
+    // the records are block-uniform: said so, so that everything derived from them (buffer
+    // resources, scalar offsets) stays in scalar registers
+    auto uniform4 = [](int4 v) {
+        return int4{__builtin_amdgcn_readfirstlane(v.x), __builtin_amdgcn_readfirstlane(v.y),
+                    __builtin_amdgcn_readfirstlane(v.z), __builtin_amdgcn_readfirstlane(v.w)};
+    };
+    const int4 d = uniform4(a.ws_desc[2 * x]);
+    const int4 cv = uniform4(a.ws_desc[2 * x + 1]);
+    // short band of workgroup x: all of its pieces at once (loading pieces before the
+    // record arrives was measured: no faster, and it reads pieces that most blocks --
+    // those owning no short band -- never use)
     for (int idx = threadIdx.x; idx < rows * C4; idx += kMergeThreads) {
+        const int n = d.z;
+        if (n <= 0 || n > kShortMerge) break;
         const int row = idx / C4;
         const int c = idx - row * C4;
-        float pm[kSpec + 1], pl[kSpec + 1];
-        float4_t pa[kSpec + 1];
-        // [0]: first piece on side 1; [p]: piece p on side 0 (p = 0 is the first piece's side 0)
+        const uint32_t lacc = (uint32_t)row * acc_row + 16u * c;
+        const uint32_t lml = (uint32_t)row * 8u;
+        float4_t pa[kShortMerge];
+        f32x2_t pml[kShortMerge];
+        auto load_piece = [&](int p, int side) {
+            pa[p] = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(racc0, (int)lacc, piece_off(p, side, acc_wg, acc_row), 0));
+            pml[p] = __builtin_bit_cast(f32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rml0, (int)lml, piece_off(p, side, ml_wg, 8u), 0));
+        };
+        // pieces past the band's last are data of later workgroups (or zeros past the
+        // resource); they are masked below
+        load_piece(0, d.w);
 #pragma unroll
-        for (int p = 0; p <= kSpec; ++p) {
-            const int xw = min(x + (p == kSpec ? 0 : p), n_wg - 1);
-            const size_t r = ((size_t)xw * 2 + (p == kSpec ? 1 : 0)) * rows + row;
-            pa[p] = reinterpret_cast<const float4_t*>(a.ws_acc + r * D)[c];
-            const float2 ml = reinterpret_cast<const float2*>(a.ws_ml)[r];
-            pm[p] = ml.x;
-            pl[p] = ml.y;
-        }
-        if (d.z <= 0 || d.z > kShortMerge) continue;
-        if (d.w) {   // the first piece is on side 1
-            pa[0] = pa[kSpec];
-            pm[0] = pm[kSpec];
-            pl[0] = pl[kSpec];
+        for (int p = 1; p < kFirstPieces; ++p) load_piece(p, 0);
+        if (n > kFirstPieces) {
+#pragma unroll
+            for (int p = kFirstPieces; p < kShortMerge; ++p) load_piece(p, 0);
         }
         float M = -INFINITY;
 #pragma unroll
-        for (int p = 0; p < kSpec; ++p)
-            if (p < d.z) M = fmaxf(M, pm[p]);
-        // pieces past the speculated ones
-        for (int p = kSpec; p < d.z; ++p) M = fmaxf(M, a.ws_ml[2 * (((size_t)(x + p) * 2) * rows + row)]);
+        for (int p = 0; p < kShortMerge; ++p)
+            if (p < n) M = fmaxf(M, pml[p].x);
         float Ls = 0.f;
         float4_t o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int p = 0; p < kSpec; ++p)
-            if (p < d.z) {
-                const float e = fast_exp2(pm[p] - M);   // 0 for an empty piece
-                Ls += e * pl[p];
+        for (int p = 0; p < kShortMerge; ++p)
+            if (p < n) {
+                const float e = fast_exp2(pml[p].x - M);   // 0 for an empty piece
+                Ls += e * pml[p].y;
                 o += e * pa[p];
             }
-        for (int p = kSpec; p < d.z; ++p) {
-            const size_t r = ((size_t)(x + p) * 2) * rows + row;
-            const float e = fast_exp2(a.ws_ml[2 * r] - M);
-            Ls += e * a.ws_ml[2 * r + 1];
-            o += e * reinterpret_cast<const float4_t*>(a.ws_acc + r * D)[c];
-        }
-        reinterpret_cast<float4_t*>(a.out + out_row(d, row) * D)[c] = o / Ls;
+        reinterpret_cast<float4_t*>(a.out + out_row(d.x, d.y, row) * D)[c] = o / Ls;
     }
-    // Rows of long bands: long row k (the row-th row of the j-th long record in workgroup
-    // order, k = j * rows + row) goes to block k % gridDim.x.  The long records are found
-    // with ballots (kMaxBalancedWG records at most, kMergeThreads per round), in order.
-    __shared__ int s_long[kMaxBalancedWG];   // workgroup of the j-th long record
-    __shared__ int s_wcount[kMergeThreads / 64];
-    __shared__ int s_nlong;
-    const int lane = threadIdx.x & 63;
-    const int wv = threadIdx.x >> 6;
-    int base = 0;
-#pragma unroll
-    for (int q = 0; q < kScan; ++q) {
-        const int w0 = q * kMergeThreads;
-        if (w0 >= n_wg) break;
-        const bool is_long = nz[q] > kShortMerge;
-        const uint64_t bal = __builtin_amdgcn_ballot_w64(is_long);
-        const int before = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-        if (lane == 0) s_wcount[wv] = __popcll(bal);
-        __syncthreads();
-        int off = base, total = 0;
-        for (int v = 0; v < kMergeThreads / 64; ++v) {
-            if (v < wv) off += s_wcount[v];
-            total += s_wcount[v];
+    // Long bands: the one this workgroup owns (t = 0, rows 0, n, ...) and the one that
+    // covers its start (t = 1, rows j, j + n, ...).  One call site of combine_rows.
+#pragma unroll 1
+    for (int t = 0; t < 2; ++t) {
+        const bool own = t == 0;
+        const int n = own ? (d.z > kShortMerge ? d.z : 0) : cv.w;
+        if (n == 0) continue;
+        const int o = own ? x : (cv.z >> 1);
+        const int side = own ? d.w : (cv.z & 1);
+        const int b = own ? d.x : cv.x;
+        const int band = own ? d.y : cv.y;
+        for (int row = x - o; row < rows; row += n) {
+            const size_t r0 = ((size_t)o * 2 + side) * rows + row;
+            const size_t r1 = ((size_t)o + 1) * 2 * rows + row;
+            combine_rows<D>(a.ws_ml, a.ws_acc, r0, r1, stride, n, a.out + out_row(b, band, row) * D);
         }
-        if (is_long) s_long[off + before] = w0 + threadIdx.x;
-        base += total;
-        __syncthreads();
-    }
-    if (threadIdx.x == 0) s_nlong = base;
-    __syncthreads();
-    const int n_long_rows = s_nlong * rows;
-    for (int k = x; k < n_long_rows; k += gridDim.x) {
-        const int w = s_long[k / rows];
-        const int row = k - (k / rows) * rows;
-        const int4 d = a.ws_desc[w];
-        const size_t r0 = ((size_t)w * 2 + d.w) * rows + row;
-        const size_t r1 = ((size_t)w + 1) * 2 * rows + row;
-        combine_rows<D>(a.ws_ml, a.ws_acc, r0, r1, stride, d.z, a.out + out_row(d, row) * D);
     }
 }
 

@@ -102,10 +102,10 @@ def ws_size(**over):
 def test_workspace_size():
     # no partition size, no flag: balanced route.  Per workgroup (up to 1024): two sides x
     # the streams read side by side (2 KV heads here) x heads_per_wg rows of (D + 2)
-    # floats, plus a 16-byte record.  Group 4 -> 4 heads per wave.
-    assert ws_size() == 1024 * 2 * 2 * 4 * (128 + 2) * 4 + 1024 * 16
+    # floats, plus two 16-byte records.  Group 4 -> 4 heads per wave.
+    assert ws_size() == 1024 * 2 * 2 * 4 * (128 + 2) * 4 + 1024 * 32
     # 4 KV heads side by side, group 6 -> 6 heads per wave
-    assert ws_size(query_heads=24, kv_heads=4) == 1024 * 2 * 4 * 6 * (128 + 2) * 4 + 1024 * 16
+    assert ws_size(query_heads=24, kv_heads=4) == 1024 * 2 * 4 * 6 * (128 + 2) * 4 + 1024 * 32
     # fixed partitions of one page -> 8 partitions of (D + 2) floats per (sequence, head)
     assert ws_size(partition_size=16) == 2 * 8 * 8 * (128 + 2) * 4
     assert ws_size(partition_size=16, max_context_length=40) == 2 * 8 * 3 * (128 + 2) * 4
