@@ -804,7 +804,10 @@ pa_decode_balanced(DecodeArgs a) {
     const int sp = wave - rr * SPW;           // this wave's stream within a band
     const int li = sp * RW + rr;
 
-    if (tid < NS) s_meta[tid][0] = -1;
+    if (tid < NS) {
+        s_meta[tid][0] = -1;
+        s_meta[tid][2] = -1;
+    }
     const int plane = tile_prefix<NT>(a.ctx, B, s_pref, s_ctx, s_wsum);
 
     // empty sequences: a zero output, written by one workgroup each
@@ -952,6 +955,56 @@ pa_decode_balanced(DecodeArgs a) {
         }
     };
 
+    // A wave's two partial slots (2 li, 2 li + 1) start empty -- weight 0, zero sums --
+    // so that the combine at the end can fold every slot of a run without first asking
+    // which were written.  Done while the wave's first tile's loads are in flight.
+    auto clear_my_slots = [&]() {
+        for (int i = L.lane; i < 2 * HP * C4; i += 64) {
+            const int sl = 2 * li + i / (HP * C4);
+            const int rest = i % (HP * C4);
+            s_acc[sl][rest / C4][rest % C4] = float4_t{0.f, 0.f, 0.f, 0.f};
+        }
+        if (L.lane < 2 * HP) {
+            s_m[2 * li + L.lane / HP][L.lane % HP] = -INFINITY;
+            s_l[2 * li + L.lane / HP][L.lane % HP] = 0.f;
+        }
+    };
+    // The workgroup's two merge records, written by lane 0 of the last wave while its
+    // first tile's loads are in flight (or after the loop when it has no tile): they
+    // depend only on the split, and computing them costs one lane about a microsecond.
+    auto write_records = [&]() {
+        if (L.lane != 0) return;
+        // [0]: the band holding the last unit, if it starts here and goes on --
+        // {sequence, band, pieces n, side of the first piece}; the pieces are this
+        // workgroup's and one per following workgroup up to the one holding the band's
+        // last unit.  [1]: the band holding the first unit, if that band started in an
+        // earlier workgroup o and is long (n > kShortMerge): this workgroup's merge block
+        // then combines some of its rows -- {sequence, band, 2 o + side of o's piece, n};
+        // n = 0 otherwise.
+        int4 own = {0, 0, 0, 0};
+        int4 cov = {0, 0, 0, 0};
+        if (g1 > g0) {
+            int b, band, lt;
+            locate_unit(g1 - 1, B, SG, s_pref, b, band, lt);
+            const int Tb = s_pref[b + 1] - s_pref[b];
+            const int S0 = SG * s_pref[b] + band * Tb;
+            const int E = S0 + Tb;
+            if (E > g1 && S0 >= g0) own = int4{b, band, wg_of_unit(E - 1, N, NWG) - w + 1, S0 == g0 ? 0 : 1};
+        }
+        if (g0 < N) {
+            int b, band, lt;
+            locate_unit(g0, B, SG, s_pref, b, band, lt);
+            const int Tb = s_pref[b + 1] - s_pref[b];
+            const int S0 = SG * s_pref[b] + band * Tb;
+            if (S0 < g0) {
+                const int o = wg_of_unit(S0, N, NWG);
+                const int n = wg_of_unit(S0 + Tb - 1, N, NWG) - o + 1;
+                if (n > kShortMerge) cov = int4{b, band, 2 * o + (S0 == split_point(o, N, NWG) ? 0 : 1), n};
+            }
+        }
+        a.ws_desc[2 * w] = own;
+        a.ws_desc[2 * w + 1] = cov;
+    };
     if (nk > 0) {
         // DEPTH register buffers: tile i + DEPTH - 1 is loaded before tile i is consumed.
         // The loop runs a multiple of DEPTH tiles and has no exit in its middle (see the
@@ -991,6 +1044,10 @@ pa_decode_balanced(DecodeArgs a) {
                 if constexpr (DEPTH == 1) load_tile(min(inext, nk - 1), dsc[nxt], kb[nxt], vb[nxt], qb);
                 else load_tile(min(inext, nk - 1), dsc[nxt], kb[nxt], vb[nxt], qr[nxt]);
                 __builtin_amdgcn_sched_barrier(0);
+                if (i + d == 0) {
+                    clear_my_slots();
+                    if (wave == NW - 1) write_records();
+                }
                 if constexpr (DEPTH == 1) consume(dsc[d], kb[d], vb[d], qb, i + d);
                 else if (i + d < nk) consume(dsc[d], kb[d], vb[d], qr[d], i + d);
                 else __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // see below
@@ -1006,8 +1063,7 @@ pa_decode_balanced(DecodeArgs a) {
 
     // Runs of slots: the non-empty slots of one stream are adjacent (waves of one stream
     // are adjacent, slots are in unit order and a band's units are contiguous).  Wave 0
-    // finds where each run starts; meanwhile the last wave writes the workgroup's merge
-    // record.
+    // finds where each run starts.
     if (wave == 0) {
         const int lane = L.lane;
         const int sid = lane < NS ? s_meta[lane][0] : -1;
@@ -1030,37 +1086,9 @@ pa_decode_balanced(DecodeArgs a) {
             s_nruns = nr;
         }
     }
-    if (wave == NW - 1 && L.lane == 0) {
-        // The workgroup's two merge records.  [0]: the band holding its last unit, if it
-        // starts here and goes on -- {sequence, band, pieces n, side of the first piece};
-        // the pieces are this workgroup's and one per following workgroup up to the one
-        // holding the band's last unit.  [1]: the band holding its first unit, if that
-        // band started in an earlier workgroup o and is long (n > kShortMerge): this
-        // workgroup's merge block then combines some of its rows -- {sequence, band,
-        // 2 o + side of o's piece, n}; n = 0 otherwise.
-        int4 own = {0, 0, 0, 0};
-        int4 cov = {0, 0, 0, 0};
-        if (g1 > g0) {
-            int b, band, lt;
-            locate_unit(g1 - 1, B, SG, s_pref, b, band, lt);
-            const int Tb = s_pref[b + 1] - s_pref[b];
-            const int S0 = SG * s_pref[b] + band * Tb;
-            const int E = S0 + Tb;
-            if (E > g1 && S0 >= g0) own = int4{b, band, wg_of_unit(E - 1, N, NWG) - w + 1, S0 == g0 ? 0 : 1};
-        }
-        if (g0 < N) {
-            int b, band, lt;
-            locate_unit(g0, B, SG, s_pref, b, band, lt);
-            const int Tb = s_pref[b + 1] - s_pref[b];
-            const int S0 = SG * s_pref[b] + band * Tb;
-            if (S0 < g0) {
-                const int o = wg_of_unit(S0, N, NWG);
-                const int n = wg_of_unit(S0 + Tb - 1, N, NWG) - o + 1;
-                if (n > kShortMerge) cov = int4{b, band, 2 * o + (S0 == split_point(o, N, NWG) ? 0 : 1), n};
-            }
-        }
-        a.ws_desc[2 * w] = own;
-        a.ws_desc[2 * w + 1] = cov;
+    if (nk == 0) {
+        clear_my_slots();
+        if (wave == NW - 1) write_records();
     }
     if (g1 == g0) {
         // no units: empty triples (weight 0) for a merge whose band spans this
@@ -1095,21 +1123,44 @@ pa_decode_balanced(DecodeArgs a) {
             const int s0 = s_runs[r], s1 = s_runs[r + 1];
             const int sid = s_meta[s0][0];
             const int tb = s_meta[s0][1];
-            int te = s_meta[s0][2];
+            int te = -1;
             float M = -INFINITY;
-            for (int s = s0; s < s1; ++s)
-                if (s_meta[s][0] >= 0) {
-                    M = fmaxf(M, s_m[s][h]);
-                    te = s_meta[s][2];
-                }
             float Ls = 0.f;
             float4_t o = {0.f, 0.f, 0.f, 0.f};
-            for (int s = s0; s < s1; ++s)
-                if (s_meta[s][0] >= 0) {
-                    const float f = fast_exp2(s_m[s][h] - M);
-                    Ls += f * s_l[s][h];
-                    o += f * s_acc[s][h][d4];
+            // Up to KF slots (two per wave, three waves per stream) are read all at once;
+            // empty slots inside the run fold in with weight 0, and lanes past the run's end
+            // re-read its first slot with weight 0.
+            constexpr int KF = 6;
+            if (s1 - s0 <= KF) {
+                float mk[KF], lk[KF];
+                float4_t ak[KF];
+#pragma unroll
+                for (int k = 0; k < KF; ++k) {
+                    const bool in = s0 + k < s1;
+                    const int sl = in ? s0 + k : s0;
+                    mk[k] = in ? s_m[sl][h] : -INFINITY;
+                    lk[k] = s_l[sl][h];
+                    ak[k] = s_acc[sl][h][d4];
+                    te = max(te, in ? s_meta[sl][2] : -1);
+                    M = fmaxf(M, mk[k]);
                 }
+#pragma unroll
+                for (int k = 0; k < KF; ++k) {
+                    const float f = fast_exp2(mk[k] - M);
+                    Ls += f * lk[k];
+                    o += f * ak[k];
+                }
+            } else {
+                for (int sl = s0; sl < s1; ++sl) {
+                    M = fmaxf(M, s_m[sl][h]);
+                    te = max(te, s_meta[sl][2]);
+                }
+                for (int sl = s0; sl < s1; ++sl) {
+                    const float f = fast_exp2(s_m[sl][h] - M);
+                    Ls += f * s_l[sl][h];
+                    o += f * s_acc[sl][h][d4];
+                }
+            }
             const int b = sid / S;
             const int strm = sid - b * S;
             const int band = strm / SPW;
