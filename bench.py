@@ -366,6 +366,17 @@ def main():
     avg_launch_ms = region_ms / args.steps
     achieved = kv_bytes / (avg_launch_ms * 1e-3) / 1e9
 
+    # distribution of single calls: an event pair around each call, calls back to back
+    n_single = min(args.steps, 200)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n_single)]
+    for i, (e0, e1) in enumerate(evs):
+        e0.record(stream)
+        step(i)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    single_us = np.array([e0.elapsed_time(e1) * 1e3 for e0, e1 in evs])
+
     append_line = measure_append(dec, wl, ks[0], vs[0], bt, stream, args.append_steps)
 
     if args.copy_calibration:
@@ -417,6 +428,7 @@ def main():
             "traffic": traffic,
             "kernel": kernel_name,
             "avg_launch_us": round(avg_launch_ms * 1e3, 3),
+            "call_us_p10_median_p90": [round(float(np.percentile(single_us, q)), 3) for q in (10, 50, 90)],
             "timing": f"HIP events on the call's stream around {args.steps} back-to-back calls",
         },
     }
