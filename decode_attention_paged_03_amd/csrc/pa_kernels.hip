@@ -84,7 +84,7 @@ constexpr uint32_t kOutOfRange = 0x7FFFFF00u;
 #define PA_KROW 1    // balanced route: load K in whole rows and regroup them through LDS
 #endif
 #ifndef PA_RUN_SKEW
-#define PA_RUN_SKEW 10   // balanced route: percent by which early rounds of waves get more work
+#define PA_RUN_SKEW 20   // balanced route: percent by which early rounds of waves get more work
 #endif
 #ifndef PA_BAL_PRIO
 #define PA_BAL_PRIO 1    // balanced route: raise the issue priority of waves that fall behind
