@@ -9,7 +9,8 @@
 //    of a page (the KV heads of a token sit next to each other) and the memory channels
 //    are loaded evenly.  Bands are laid end to end; workgroup w takes the units
 //    [w N / W, (w+1) N / W) of the N (band, 16-token tile) units, and the waves reading
-//    one stream split that range in equal runs.  A stream that a wave holds entirely is
+//    one stream split that range in runs, the earlier rounds of waves taking somewhat
+//    more (they are issued first).  A stream that a wave holds entirely is
 //    finished there (the single-tile path of the "paged_attention_v2_pytorch.py" commit
 //    page); pieces of a stream that crosses waves are combined in LDS, and pieces that
 //    cross workgroups leave (max, sum, acc) triples for pa_merge_balanced -- the
@@ -17,7 +18,8 @@
 //    paged attention", with the split points chosen for balance instead of fixed.
 //  * Fixed partitions (a partition size or a flag given): one workgroup per (sequence,
 //    KV head, head chunk, partition of partition_size tokens), partition triples in the
-//    workspace, pa_merge_kernel per (sequence, query head) -- p2's PARTITION_SIZE scheme.
+//    workspace, pa_merge_kernel per (sequence, query head) -- the PARTITION_SIZE scheme of
+//    the "paged_attention_v2_pytorch.py" commit page.
 //
 // Both combine triples as M = max m_p, L = sum exp(m_p - M) l_p,
 // out = sum exp(m_p - M) acc_p / L (the V4 merge kernel's combination, with the global
@@ -99,7 +101,7 @@ struct DecodeArgs {
     float* out;
     float* ws_acc;          // partial rows of D floats
     float* ws_ml;           // partial rows' (max in log2 units, sum)
-    int4* ws_desc;          // balanced route: per-workgroup merge record
+    int4* ws_desc;          // balanced route: two merge records per workgroup
     float scale_log2;       // |scale| * log2(e)
     uint32_t q_sign;        // 0x80008000 to negate q (negative scale), else 0
     int batch, query_heads, kv_heads, group, n_chunks, max_pages, partition, n_part_max, ps_log2;

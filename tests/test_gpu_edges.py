@@ -125,3 +125,27 @@ def test_max_context_length_bound(partition):
         dec.close()
     C.check_against_oracle(out, C.oracle.attend_workload(wl, nthreads=C.oracle_threads()),
                            f"max_context_length partition {partition}")
+
+
+def test_concurrent_streams_distinct_workspaces():
+    """Two calls in flight at once on two streams, each with its own handle and workspace
+    (the documented rule for concurrency), give the same bits as the calls made one after
+    the other."""
+    import torch
+    wls = [W.make_named("small_batch"), W.make_named("tiny")]
+    devs = [C.Device(w) for w in wls]
+    decs = [pa.decoder_for(w) for w in wls]
+    try:
+        ref = [dev.run(dec).clone() for dev, dec in zip(devs, decs)]
+        streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+        outs = [torch.full_like(r, float("nan")) for r in ref]
+        torch.cuda.synchronize()
+        for _ in range(3):
+            for wl_, dev, dec, s, out in zip(wls, devs, decs, streams, outs):
+                dec(dev.q, dev.k, dev.v, dev.bt, dev.ctx, wl_.scale, out=out, stream=s)
+        torch.cuda.synchronize()
+        for r, out in zip(ref, outs):
+            assert torch.equal(r.view(torch.int32), out.view(torch.int32))
+    finally:
+        for d in decs:
+            d.close()
