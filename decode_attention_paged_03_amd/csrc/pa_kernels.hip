@@ -1320,14 +1320,29 @@ int balanced_grid() {
     return cus < kMaxBalancedWG ? cus : kMaxBalancedWG;
 }
 
+// LDS a gfx950 workgroup may use (the CU's 160 KB).
+constexpr size_t kLdsPerWorkgroup = 160 * 1024;
+
+// Static LDS bytes of a kernel (host-side query; nothing is enqueued).
+template <typename K>
+size_t static_lds_bytes(K kern) {
+    hipFuncAttributes attr{};
+    if (hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(kern)) != hipSuccess) return SIZE_MAX;
+    return attr.sharedSizeBytes;
+}
+
 template <int D, int HP, int NW, bool SPLIT>
 hipError_t launch_balanced_nw(const Plan& pl, const DecodeArgs& args, hipStream_t stream) {
-    // Whole-row K loads (staged through LDS): measured faster with up to 4 heads per wave
-    // (serving shape: -1.1 us per call) and slower with 6 (long context: +1.2 us), where
-    // the LDS round trip lengthens each tile more than the wider loads save.
-    constexpr bool krow = PA_KROW && D == 128 && HP <= 4;
-    const auto kern = pa_decode_balanced<D, HP, kBalDepth, NW, SPLIT, krow>;
+    // Whole-row K loads (staged through LDS) were measured faster at every head count
+    // (serving shape with 4 heads per wave: -1.1 us per call; long context, 6 heads:
+    // -0.7 us; mixed batch, 8 heads: -3 us).  Their 52 KB of staging is used when the
+    // kernel's LDS still fits next to the per-sequence arrays; otherwise K is loaded in
+    // the MFMA layout.
+    const auto kern_row = pa_decode_balanced<D, HP, kBalDepth, NW, SPLIT, PA_KROW && D == 128>;
+    const auto kern_mfma = pa_decode_balanced<D, HP, kBalDepth, NW, SPLIT, false>;
     const size_t lds = (size_t)(2 * pl.prob.batch + 1) * sizeof(int);
+    static const size_t row_static = static_lds_bytes(kern_row);
+    const auto kern = (row_static != SIZE_MAX && row_static + lds <= kLdsPerWorkgroup) ? kern_row : kern_mfma;
     const int grid = balanced_grid();
     if (grid <= 0) return hipErrorInvalidDevice;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NW * 64), lds, stream, args);

@@ -149,3 +149,16 @@ def test_concurrent_streams_distinct_workspaces():
     finally:
         for d in decs:
             d.close()
+
+
+@pytest.mark.parametrize("batch", [96, 1500])
+def test_eight_heads_per_wave_both_k_layouts(batch):
+    """Eight query heads per wave: with a moderate batch the kernel stages K rows through
+    LDS; with 1500 sequences the per-sequence arrays leave no room for that staging and
+    K is loaded in the MFMA layout instead.  Both agree with the oracle."""
+    rng = np.random.default_rng(7700 + batch)
+    ctx = rng.integers(1, 300, size=batch)
+    wl = W.make_workload(name="g8", batch=batch, query_heads=16, kv_heads=2, head_dim=128,
+                         page_size=16, context_lengths=list(ctx), pool="holes10",
+                         seed=7701 + batch)
+    C.decode_and_check(wl, what=f"8 heads per wave, batch {batch}")
