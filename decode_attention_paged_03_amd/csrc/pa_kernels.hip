@@ -550,10 +550,34 @@ struct MergeArgs {
 };
 
 constexpr int kMergeThreads = 512;
-// Balanced route: a band whose pieces span at most this many workgroups is merged by the
-// block of the workgroup where it starts, all pieces at once; longer bands have their
-// rows dealt out over the blocks of the workgroups they span.
+// Balanced route: the merge tasks of a band (one row, kSliceCols float4 columns: 128
+// bytes) are dealt over the blocks of the workgroups the band spans.  In a band of at most
+// kShortMerge pieces one thread loads all pieces of its column; in longer bands a thread
+// takes kLongUnroll of them.
 constexpr int kShortMerge = 16;
+constexpr int kSliceCols = 8;
+constexpr int kLongUnroll = 8;
+// a lane offset past every merge resource (at most 2^31 - 2^24 bytes, so that adding a
+// piece offset cannot wrap past 2^32)
+constexpr uint32_t kPastRange = 0x7F000000u;
+
+// a compile-time int carried by a value (for generic lambdas)
+template <int N>
+struct IntC {
+    static constexpr int value = N;
+};
+
+// (m, l, o) <- the combination of two (max, sum, acc) triples; a triple with maximum
+// -inf weighs nothing, and two of them give (-inf, 0, 0).
+__device__ __forceinline__ void fold_triple(float& m, float& l, float4_t& o, float m2, float l2, float4_t o2) {
+    const float M = fmaxf(m, m2);
+    const float Ms = M == -INFINITY ? 0.f : M;
+    const float a1 = fast_exp2(m - Ms);
+    const float a2 = fast_exp2(m2 - Ms);
+    l = a1 * l + a2 * l2;
+    o = a1 * o + a2 * o2;
+    m = M;
+}
 
 // Combination of n (max, sum, acc) triples of one output row: out = sum_p e_p acc_p /
 // sum_p e_p l_p with e_p = exp2(m_p - max m).  Triple p is row r(p) of the workspace
@@ -980,9 +1004,8 @@ pa_decode_balanced(DecodeArgs a) {
         // {sequence, band, pieces n, side of the first piece}; the pieces are this
         // workgroup's and one per following workgroup up to the one holding the band's
         // last unit.  [1]: the band holding the first unit, if that band started in an
-        // earlier workgroup o and is long (n > kShortMerge): this workgroup's merge block
-        // then combines some of its rows -- {sequence, band, 2 o + side of o's piece, n};
-        // n = 0 otherwise.
+        // earlier workgroup o: this workgroup's merge block then takes a share of its
+        // tasks -- {sequence, band, 2 o + side of o's piece, n}; n = 0 otherwise.
         int4 own = {0, 0, 0, 0};
         int4 cov = {0, 0, 0, 0};
         if (g1 > g0) {
@@ -1001,7 +1024,7 @@ pa_decode_balanced(DecodeArgs a) {
             if (S0 < g0) {
                 const int o = wg_of_unit(S0, N, NWG);
                 const int n = wg_of_unit(S0 + Tb - 1, N, NWG) - o + 1;
-                if (n > kShortMerge) cov = int4{b, band, 2 * o + (S0 == split_point(o, N, NWG) ? 0 : 1), n};
+                cov = int4{b, band, 2 * o + (S0 == split_point(o, N, NWG) ? 0 : 1), n};
             }
         }
         a.ws_desc[2 * w] = own;
@@ -1192,44 +1215,42 @@ pa_decode_balanced(DecodeArgs a) {
 // has exactly one owner); the pieces of stream sp, head h of such a band are rows
 // r(0) = ((w * 2 + side) * spw + sp) * HP + h and r(p) = r(0) + p * 2 * spw * HP rows
 // of side 0 of the following workgroups.  Merge block x reads workgroup x's two records
-// (written by the decode kernel, no search here):
-//   * a short band it owns (n <= kShortMerge): one thread per (row, float4 column), all
-//     pieces at once;
-//   * rows of long bands: the n blocks of the workgroups a long band spans take rows
-//     j, j + n, ... (j = x - owner), each row with all threads of the block, so the
-//     rows of one long band are spread over the machine.
+// (written by the decode kernel, no search here): the band it owns and the band that
+// covers its first unit.  A band spanning n workgroups has rows x (D / 32) tasks -- one
+// row, 128 bytes of columns -- and block o + j of its n blocks takes the j-th of n equal
+// shares, so the loads of every band are spread over all blocks it spans:
+//   * bands of at most kShortMerge pieces: one thread per (task, float4 column) loads all
+//     pieces at once; the block's shares of both its bands go in one pass;
+//   * longer bands: the pieces of a task are split over groups of kLongUnroll, one group
+//     per thread, and the groups are combined through lane shuffles (and LDS when a task
+//     spans several waves).
+// Every load of a pass is issued before any of its results is used: one round trip per
+// pass.
 template <int D, int HP>
 __global__ void __launch_bounds__(kMergeThreads)
 pa_merge_balanced(DecodeArgs a, int n_wg) {
     constexpr int C4 = D / 4;
+    constexpr int SC = kSliceCols;                  // float4 columns per task
+    constexpr int NSL = C4 / SC;                    // tasks per row
+    static_assert(C4 % SC == 0, "a row is a whole number of tasks");
+    (void)n_wg;
     const int x = blockIdx.x;
-    const int spw = a.spw;
-    const int rows = spw * HP;
-    const size_t stride = (size_t)2 * rows;
-    auto out_row = [&](int b, int band, int row) {
+    const int tid = threadIdx.x;
+    const int rows = a.spw * HP;
+    const int T = rows * NSL;                       // tasks of one band
+    const uint32_t row_bytes = (uint32_t)D * 4u;
+    const uint32_t acc_wg = (uint32_t)(2 * rows) * row_bytes;      // bytes per workgroup
+    const uint32_t ml_wg = (uint32_t)(2 * rows) * 8u;
+    const char* acc0 = reinterpret_cast<const char*>(a.ws_acc);
+    const char* ml0 = reinterpret_cast<const char*>(a.ws_ml);
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    auto out_ptr = [&](int b, int band, int row, int col4) {
         const int sp = row / HP;
         const int h = row - sp * HP;
-        const int s = band * spw + sp;
+        const int s = band * a.spw + sp;
         const int kvh = s / a.n_chunks;
         const int chunk = s - kvh * a.n_chunks;
-        return (size_t)b * a.query_heads + kvh * a.group + chunk * HP + h;
-    };
-    constexpr int kFirstPieces = 4;   // pieces loaded for every short band (more if needed)
-    typedef float f32x2_t __attribute__((ext_vector_type(2)));
-    // Pieces of a band owned by workgroup x, relative to its first row (x * 2) * rows:
-    // piece 0 at side * rows rows, piece p >= 1 at p * 2 * rows rows (side 0 of workgroup
-    // x + p).  One buffer resource spans them; the lane's (row, column) part of an offset
-    // is a register, the piece's part a scalar.
-    const uint32_t acc_row = (uint32_t)(D * 4);
-    const uint32_t acc_wg = (uint32_t)(2 * rows) * acc_row;        // bytes per workgroup
-    const uint32_t ml_wg = (uint32_t)(2 * rows) * 8u;
-    const char* acc_base = reinterpret_cast<const char*>(a.ws_acc) + (size_t)x * acc_wg;
-    const char* ml_base = reinterpret_cast<const char*>(a.ws_ml) + (size_t)x * ml_wg;
-    const int span = min(kShortMerge, n_wg - x);                    // workgroups x .. x + span - 1
-    const __amdgpu_buffer_rsrc_t racc0 = tile_rsrc(acc_base, (int)(span * acc_wg));
-    const __amdgpu_buffer_rsrc_t rml0 = tile_rsrc(ml_base, (int)(span * ml_wg));
-    auto piece_off = [&](int p, int side, uint32_t per_wg, uint32_t per_row) {   // wave-uniform
-        return __builtin_amdgcn_readfirstlane((int)(p == 0 ? (uint32_t)side * (uint32_t)rows * per_row : (uint32_t)p * per_wg));
+        return reinterpret_cast<float4_t*>(a.out + ((size_t)b * a.query_heads + kvh * a.group + chunk * HP + h) * D) + col4;
     };
     // the records are block-uniform: said so, so that everything derived from them (buffer
     // resources, scalar offsets) stays in scalar registers
@@ -1237,63 +1258,204 @@ pa_merge_balanced(DecodeArgs a, int n_wg) {
         return int4{__builtin_amdgcn_readfirstlane(v.x), __builtin_amdgcn_readfirstlane(v.y),
                     __builtin_amdgcn_readfirstlane(v.z), __builtin_amdgcn_readfirstlane(v.w)};
     };
-    const int4 d = uniform4(a.ws_desc[2 * x]);
-    const int4 cv = uniform4(a.ws_desc[2 * x + 1]);
-    // short band of workgroup x: all of its pieces at once (loading pieces before the
-    // record arrives was measured: no faster, and it reads pieces that most blocks --
-    // those owning no short band -- never use)
-    for (int idx = threadIdx.x; idx < rows * C4; idx += kMergeThreads) {
-        const int n = d.z;
-        if (n <= 0 || n > kShortMerge) break;
-        const int row = idx / C4;
-        const int c = idx - row * C4;
-        const uint32_t lacc = (uint32_t)row * acc_row + 16u * c;
-        const uint32_t lml = (uint32_t)row * 8u;
-        float4_t pa[kShortMerge];
-        f32x2_t pml[kShortMerge];
-        auto load_piece = [&](int p, int side) {
-            pa[p] = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(racc0, (int)lacc, piece_off(p, side, acc_wg, acc_row), 0));
-            pml[p] = __builtin_bit_cast(f32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rml0, (int)lml, piece_off(p, side, ml_wg, 8u), 0));
-        };
-        // pieces past the band's last are data of later workgroups (or zeros past the
-        // resource); they are masked below
-        load_piece(0, d.w);
+    const int4 d = uniform4(a.ws_desc[2 * x]);      // own band {b, band, n, side}, n = 0: none
+    const int4 cv = uniform4(a.ws_desc[2 * x + 1]); // covering band {b, band, 2 o + side, n}
+    const int n_o = d.z, n_c = cv.w;
+    const int o_c = cv.z >> 1;
+    const int own_hi = n_o > 0 ? T / n_o : 0;       // own share: tasks [0, own_hi)
+    const int cov_lo = n_c > 0 ? (x - o_c) * T / n_c : 0;
+    const int cov_hi = n_c > 0 ? (x - o_c + 1) * T / n_c : 0;
+    const bool own_short = n_o > 0 && n_o <= kShortMerge;
+    const bool cov_short = n_c > 0 && n_c <= kShortMerge;
+
+    // Short bands: both shares in one list of tasks, one thread per (task, column).  The
+    // pieces of both bands lie in workgroups base .. end - 1 (a covering band that goes on
+    // past x leaves x no band of its own), one buffer resource spans them; the lane's
+    // (band, row, column) part of an offset is a register, the piece's a scalar.
+    if (own_short || cov_short) {
+        const int na = own_short ? own_hi : 0;
+        const int tot = na + (cov_short ? cov_hi - cov_lo : 0);
+        const int base = cov_short ? o_c : x;
+        const int end = own_short ? x + n_o : o_c + n_c;
+        const int nmax = max(own_short ? n_o : 0, cov_short ? n_c : 0);
+        const __amdgpu_buffer_rsrc_t racc = tile_rsrc(acc0 + (size_t)base * acc_wg, (int)((end - base) * acc_wg));
+        const __amdgpu_buffer_rsrc_t rml = tile_rsrc(ml0 + (size_t)base * ml_wg, (int)((end - base) * ml_wg));
+        const int col = tid % SC;
+        constexpr int TPP = kMergeThreads / SC;     // tasks per pass and task slot
+        // A thread takes KT tasks (v, v + TPP, ...) of KP pieces each (KT * KP =
+        // kShortMerge registers of pieces), all loads first: one round trip per pass.
+        auto pass = [&](auto kt, auto kp) {
+            constexpr int KT = decltype(kt)::value;
+            constexpr int KP = decltype(kp)::value;
+            for (int v0 = tid / SC; v0 < tot; v0 += TPP * KT) {
+                float4_t pa[KT][KP];
+                f32x2_t pml[KT][KP];
+                int n[KT], row[KT], col4[KT];
+                bool in_own[KT];
 #pragma unroll
-        for (int p = 1; p < kFirstPieces; ++p) load_piece(p, 0);
-        if (n > kFirstPieces) {
+                for (int j = 0; j < KT; ++j) {
+                    const int v = v0 + j * TPP;
+                    in_own[j] = v < na;
+                    const int task = in_own[j] ? v : cov_lo + (v - na);
+                    row[j] = task / NSL;
+                    col4[j] = (task - row[j] * NSL) * SC + col;
+                    const int o = in_own[j] ? x : o_c;
+                    const int side = in_own[j] ? d.w : (cv.z & 1);
+                    n[j] = v < tot ? (in_own[j] ? n_o : n_c) : 0;
+                    // a slot past the last task loads from past the resources: zeros
+                    const uint32_t la = v < tot ? (uint32_t)(o - base) * acc_wg + (uint32_t)row[j] * row_bytes + 16u * col4[j] : kPastRange;
+                    const uint32_t lm = v < tot ? (uint32_t)(o - base) * ml_wg + (uint32_t)row[j] * 8u : kPastRange;
+                    pa[j][0] = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(racc, (int)(la + (uint32_t)side * rows * row_bytes), 0, 0));
+                    pml[j][0] = __builtin_bit_cast(f32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rml, (int)(lm + (uint32_t)side * rows * 8u), 0, 0));
+                    // Pieces past a band's last are zeros past the resource or data of
+                    // other workgroups; they are masked below.  (Scalar offsets are
+                    // wave-uniform; readfirstlane keeps the compiler from carrying them in
+                    // vector registers.  The whole vector is reinterpreted: bit-casting
+                    // single elements of the load's result made clang read one dword for
+                    // both.)
 #pragma unroll
-            for (int p = kFirstPieces; p < kShortMerge; ++p) load_piece(p, 0);
-        }
-        float M = -INFINITY;
+                    for (int p = 1; p < KP; ++p) {
+                        pa[j][p] = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(racc, (int)la, __builtin_amdgcn_readfirstlane((int)(p * acc_wg)), 0));
+                        pml[j][p] = __builtin_bit_cast(f32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rml, (int)lm, __builtin_amdgcn_readfirstlane((int)(p * ml_wg)), 0));
+                    }
+                }
 #pragma unroll
-        for (int p = 0; p < kShortMerge; ++p)
-            if (p < n) M = fmaxf(M, pml[p].x);
-        float Ls = 0.f;
-        float4_t o = {0.f, 0.f, 0.f, 0.f};
+                for (int j = 0; j < KT; ++j) {
+                    if (n[j] == 0) continue;
+                    float M = -INFINITY;
 #pragma unroll
-        for (int p = 0; p < kShortMerge; ++p)
-            if (p < n) {
-                const float e = fast_exp2(pml[p].x - M);   // 0 for an empty piece
-                Ls += e * pml[p].y;
-                o += e * pa[p];
+                    for (int p = 0; p < KP; ++p)
+                        if (p < n[j]) M = fmaxf(M, pml[j][p].x);
+                    float Ls = 0.f;
+                    float4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int p = 0; p < KP; ++p)
+                        if (p < n[j]) {
+                            const float e = fast_exp2(pml[j][p].x - M);
+                            Ls += e * pml[j][p].y;
+                            acc += e * pa[j][p];
+                        }
+                    *out_ptr(in_own[j] ? d.x : cv.x, in_own[j] ? d.y : cv.y, row[j], col4[j]) = acc / Ls;
+                }
             }
-        reinterpret_cast<float4_t*>(a.out + out_row(d.x, d.y, row) * D)[c] = o / Ls;
+        };
+        // pieces per task: the band's count rounded up to 4, 8 or 16; tasks per thread:
+        // as few as cover the block's tasks in one pass, within 16 pieces
+        static_assert(kShortMerge == 16, "the pass shapes below hold 16 pieces per thread");
+        const int slots = (tot + TPP - 1) / TPP;
+        if (nmax <= 4) {
+            if (slots <= 1) pass(IntC<1>(), IntC<4>());
+            else if (slots <= 2) pass(IntC<2>(), IntC<4>());
+            else pass(IntC<4>(), IntC<4>());
+        } else if (nmax <= 8) {
+            if (slots <= 1) pass(IntC<1>(), IntC<8>());
+            else pass(IntC<2>(), IntC<8>());
+        } else {
+            pass(IntC<1>(), IntC<16>());
+        }
     }
-    // Long bands: the one this workgroup owns (t = 0, rows 0, n, ...) and the one that
-    // covers its start (t = 1, rows j, j + n, ...).  One call site of combine_rows.
+
+    // Long bands, one at a time: a task takes SC * PG threads (PG a power of two, groups
+    // of kLongUnroll pieces), kMergeThreads / (SC * PG) tasks per pass.
+    __shared__ float s_rm[kMergeThreads / 64][SC];
+    __shared__ float s_rl[kMergeThreads / 64][SC];
+    __shared__ float4_t s_ro[kMergeThreads / 64][SC];
 #pragma unroll 1
     for (int t = 0; t < 2; ++t) {
         const bool own = t == 0;
-        const int n = own ? (d.z > kShortMerge ? d.z : 0) : cv.w;
-        if (n == 0) continue;
-        const int o = own ? x : (cv.z >> 1);
+        const int n = own ? n_o : n_c;
+        if (n <= kShortMerge) continue;
+        const int o = own ? x : o_c;
         const int side = own ? d.w : (cv.z & 1);
         const int b = own ? d.x : cv.x;
         const int band = own ? d.y : cv.y;
-        for (int row = x - o; row < rows; row += n) {
-            const size_t r0 = ((size_t)o * 2 + side) * rows + row;
-            const size_t r1 = ((size_t)o + 1) * 2 * rows + row;
-            combine_rows<D>(a.ws_ml, a.ws_acc, r0, r1, stride, n, a.out + out_row(b, band, row) * D);
+        const int lo = own ? 0 : cov_lo;
+        const int hi = own ? own_hi : cov_hi;
+        int pg2 = 1;
+        while (pg2 * kLongUnroll < n && pg2 * SC < kMergeThreads) pg2 <<= 1;
+        const int tpt = pg2 * SC;                   // threads per task
+        const int tl = tid / tpt;
+        const int pg = (tid / SC) % pg2;
+        const int col = tid % SC;
+        const int wave = tid >> 6;
+        const __amdgpu_buffer_rsrc_t racc = tile_rsrc(acc0 + (size_t)o * acc_wg, (int)(n * acc_wg));
+        const __amdgpu_buffer_rsrc_t rml = tile_rsrc(ml0 + (size_t)o * ml_wg, (int)(n * ml_wg));
+        for (int t0 = lo; t0 < hi; t0 += kMergeThreads / tpt) {
+            // threads past the last task load from past the resources: zeros, no traffic
+            const bool live = t0 + tl < hi;
+            const int task = live ? t0 + tl : lo;
+            const int row = task / NSL;
+            const int col4 = (task - row * NSL) * SC + col;
+            const uint32_t la = live ? (uint32_t)row * row_bytes + 16u * col4 : kPastRange;
+            const uint32_t lm = live ? (uint32_t)row * 8u : kPastRange;
+            float m = -INFINITY, l = 0.f;
+            float4_t acc = {0.f, 0.f, 0.f, 0.f};
+            for (int q = 0; q < n; q += pg2 * kLongUnroll) {
+                const int p0 = q + pg * kLongUnroll;                    // this thread's first piece
+                const uint32_t va = la + (p0 == 0 ? (uint32_t)side * rows * row_bytes : (uint32_t)p0 * acc_wg);
+                const uint32_t vm = lm + (p0 == 0 ? (uint32_t)side * rows * 8u : (uint32_t)p0 * ml_wg);
+                const uint32_t va1 = la + (uint32_t)p0 * acc_wg;
+                const uint32_t vm1 = lm + (uint32_t)p0 * ml_wg;
+                float4_t pa[kLongUnroll];
+                f32x2_t pml[kLongUnroll];
+                pa[0] = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(racc, (int)va, 0, 0));
+                pml[0] = __builtin_bit_cast(f32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rml, (int)vm, 0, 0));
+#pragma unroll
+                for (int k = 1; k < kLongUnroll; ++k) {
+                    pa[k] = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(racc, (int)va1, __builtin_amdgcn_readfirstlane((int)(k * acc_wg)), 0));
+                    pml[k] = __builtin_bit_cast(f32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rml, (int)vm1, __builtin_amdgcn_readfirstlane((int)(k * ml_wg)), 0));
+                }
+                // Pieces past the band's last are zeros past the resource: their maximum is
+                // made -inf, so they weigh 0.  No branch: a load used only under a branch
+                // is moved into it by the compiler, a second round trip.
+                float mk[kLongUnroll];
+                float M = m;
+#pragma unroll
+                for (int k = 0; k < kLongUnroll; ++k) {
+                    mk[k] = p0 + k < n ? pml[k].x : -INFINITY;
+                    M = fmaxf(M, mk[k]);
+                }
+                const float Ms = M == -INFINITY ? 0.f : M;
+                const float a0 = fast_exp2(m - Ms);
+                l *= a0;
+                acc *= a0;
+#pragma unroll
+                for (int k = 0; k < kLongUnroll; ++k) {
+                    const float e = fast_exp2(mk[k] - Ms);
+                    l += e * pml[k].y;
+                    acc += e * pa[k];
+                }
+                m = M;
+            }
+            // groups of one task: lanes pg * SC + col of its waves
+            for (int s = SC; s < min(64, tpt); s <<= 1) {
+                const float m2 = __shfl_xor(m, s);
+                const float l2 = __shfl_xor(l, s);
+                const float4_t o2 = {__shfl_xor(acc.x, s), __shfl_xor(acc.y, s), __shfl_xor(acc.z, s), __shfl_xor(acc.w, s)};
+                fold_triple(m, l, acc, m2, l2, o2);
+            }
+            if (tpt > 64) {                         // several waves per task: through LDS
+                if ((tid & 63) < SC) {
+                    s_rm[wave][col] = m;
+                    s_rl[wave][col] = l;
+                    s_ro[wave][col] = acc;
+                }
+                __syncthreads();
+                const int wpt = tpt / 64;
+                if (tid < (kMergeThreads / tpt) * SC) {
+                    const int w0 = (tid / SC) * wpt;
+                    m = s_rm[w0][col];
+                    l = s_rl[w0][col];
+                    acc = s_ro[w0][col];
+                    for (int k = 1; k < wpt; ++k) fold_triple(m, l, acc, s_rm[w0 + k][col], s_rl[w0 + k][col], s_ro[w0 + k][col]);
+                    const int tk = t0 + tid / SC;
+                    const int rk = tk / NSL;
+                    if (tk < hi) *out_ptr(b, band, rk, (tk - rk * NSL) * SC + col) = acc / l;
+                }
+                __syncthreads();                    // the shared arrays are reused by the next pass
+            } else if (pg == 0 && live) {
+                *out_ptr(b, band, row, col4) = acc / l;
+            }
         }
     }
 }
@@ -1338,7 +1500,8 @@ hipError_t launch_balanced_nw(const Plan& pl, const DecodeArgs& args, hipStream_
     // -0.7 us; mixed batch, 8 heads: -3 us).  Their 52 KB of staging is used when the
     // kernel's LDS still fits next to the per-sequence arrays; otherwise K is loaded in
     // the MFMA layout.
-    const auto kern_row = pa_decode_balanced<D, HP, kBalDepth, NW, SPLIT, PA_KROW && D == 128>;
+    // (the staging is per wave: with 16 waves it would not fit next to the partial slots)
+    const auto kern_row = pa_decode_balanced<D, HP, kBalDepth, NW, SPLIT, PA_KROW && D == 128 && NW <= 12>;
     const auto kern_mfma = pa_decode_balanced<D, HP, kBalDepth, NW, SPLIT, false>;
     const size_t lds = (size_t)(2 * pl.prob.batch + 1) * sizeof(int);
     static const size_t row_static = static_lds_bytes(kern_row);
