@@ -1,0 +1,101 @@
+"""GPU parity of the balanced route's merge at chosen band spans.
+
+A band (one sequence, a group of KV-head streams) that crosses workgroup boundaries
+leaves one (max, sum, acc) triple per workgroup it spans, and the merge combines them.
+The merge has two code paths -- bands of at most 16 pieces, whose threads load every
+piece of a column at once (4, 8 or 16 pieces per task), and longer bands, whose pieces
+are split over groups of threads -- and a merge block may hold a share of two bands of
+either kind.  The workloads here are chosen so that, on a 256-CU part, the largest span
+is exactly 3, 4, 5, 8, 9, 16 or 17 pieces (each side of every boundary), and so that
+blocks hold short+long, long+short, long+long and short+short pairs.  The split that
+decides the spans is modelled below on the host (units = 16-token tiles x bands, split
+evenly over the workgroups); the model is test-side bookkeeping, not the oracle.
+
+Bar: |gpu - oracle| <= 1e-3 * (1 + |oracle|), with NaN canaries never read.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from decode_attention_paged_03_amd import pa
+from decode_attention_paged_03_amd import workloads as W
+
+import gpu_common as C
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    pa.load()
+    yield
+
+
+def _spans(ctx, query_heads, kv_heads, n_wg):
+    """Pieces of every crossing band under the even split of units over n_wg workgroups."""
+    group = query_heads // kv_heads
+    hp = max(h for h in range(1, 9) if group % h == 0)   # heads per wave
+    streams = kv_heads * (group // hp)
+    bands = streams // math.gcd(streams, 12)
+    tiles = [(c + 15) // 16 for c in ctx]
+    pref = np.concatenate([[0], np.cumsum(tiles)]).astype(np.int64)
+    n = bands * int(pref[-1])
+
+    def wg_of(u):
+        return min(((u + 1) * n_wg - 1) // n, n_wg - 1)
+
+    out = []
+    for b, t in enumerate(tiles):
+        for band in range(bands if t else 0):
+            s0 = bands * int(pref[b]) + band * t
+            k = wg_of(s0 + t - 1) - wg_of(s0) + 1
+            if k > 1:
+                out.append(k)
+    return out
+
+
+def _cus():
+    import torch
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+# (query_heads, kv_heads, head_dim, batch, length, largest span on 256 CUs)
+EQUAL = [(32, 8, 128, 32, 32, 3), (32, 8, 128, 22, 32, 4), (32, 8, 128, 16, 32, 5),
+         (32, 8, 128, 10, 32, 8), (32, 8, 128, 8, 32, 9), (32, 8, 128, 7, 80, 16),
+         (32, 8, 128, 4, 32, 17), (8, 2, 64, 32, 32, 5), (8, 2, 64, 19, 32, 8),
+         (8, 2, 64, 16, 32, 9), (8, 2, 64, 9, 32, 16), (8, 2, 64, 8, 32, 17)]
+
+
+@pytest.mark.parametrize("QH,KVH,D,B,L,span", EQUAL)
+def test_equal_lengths_span(QH, KVH, D, B, L, span):
+    """Equal lengths: every crossing band spans about the same number of workgroups."""
+    ctx = [L] * B
+    sp = _spans(ctx, QH, KVH, _cus())
+    C.say(f"[case] spans {sorted(set(sp))} (target {span}), QH{QH}/KVH{KVH} D{D} B{B} L{L}")
+    if _cus() == 256:
+        assert max(sp) == span
+    wl = W.make_workload(name=f"span{span}", batch=B, query_heads=QH, kv_heads=KVH,
+                         head_dim=D, page_size=16, context_lengths=ctx, pool="holes10",
+                         seed=8100 + 7 * span + D)
+    C.decode_and_check(wl, what=f"span {span} D{D}")
+
+
+MIXED = [[3000, 60, 3000, 60, 2000], [1, 2, 700, 5000, 17, 33, 900],
+         [4000, 40, 40, 40, 40, 40, 40, 40]]
+
+
+@pytest.mark.parametrize("QH,KVH,D", [(32, 8, 128), (8, 2, 64)])
+@pytest.mark.parametrize("ctx", MIXED)
+def test_mixed_short_and_long_bands(QH, KVH, D, ctx):
+    """Long and short bands side by side: merge blocks holding a share of a short band
+    and of a long one (in either order), of two long ones, and of two short ones."""
+    sp = _spans(ctx, QH, KVH, _cus())
+    C.say(f"[case] mixed spans {sorted(set(sp))}, QH{QH}/KVH{KVH} D{D} ctx {ctx}")
+    wl = W.make_workload(name="mixed_spans", batch=len(ctx), query_heads=QH, kv_heads=KVH,
+                         head_dim=D, page_size=16, context_lengths=ctx, pool="holes10",
+                         seed=8200 + sum(ctx) % 97 + D)
+    C.decode_and_check(wl, what=f"mixed spans D{D}")
