@@ -29,6 +29,9 @@ static int gcd(int a, int b) {
 
 // Waves per balanced workgroup (12: three per SIMD, which the kernels' register use
 // allows; more waves, each with one tile in flight, keep more of the memory system busy).
+// Balanced route: below this many bands in the batch, fewer streams are read side by side.
+static constexpr long long kFewBands = 32;
+
 static int balanced_waves(int /*streams*/) {
 #ifdef PA_BAL_WAVES
     if (PA_BAL_WAVES == 8 || PA_BAL_WAVES == 12 || PA_BAL_WAVES == 16) return PA_BAL_WAVES;
@@ -105,6 +108,12 @@ int build_plan(const pa_problem* in, Plan* pl) {
         const int streams = p.kv_heads * out.n_chunks;
         out.bal_waves = balanced_waves(streams);
         out.spw = gcd(streams, out.bal_waves);
+        // With few bands in the whole batch (one long sequence, a handful of sequences),
+        // each band spans many workgroups and leaves one piece of spw x heads_per_wg rows
+        // in each: the merge then weighs most, and reading half as many streams side by
+        // side halves its rows.  With many bands, more bands per sequence cost the decode
+        // kernel more segments per wave than the merge saves.
+        if ((long long)p.batch * (streams / out.spw) < kFewBands && out.spw % 2 == 0) out.spw /= 2;
         out.waves_per_stream = out.bal_waves / out.spw;
         out.bands = streams / out.spw;
         // Rows of D floats (plus a (max, sum) pair each): per workgroup (up to

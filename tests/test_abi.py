@@ -101,11 +101,19 @@ def ws_size(**over):
 
 def test_workspace_size():
     # no partition size, no flag: balanced route.  Per workgroup (up to 1024): two sides x
-    # the streams read side by side (2 KV heads here) x heads_per_wg rows of (D + 2)
-    # floats, plus two 16-byte records.  Group 4 -> 4 heads per wave.
-    assert ws_size() == 1024 * 2 * 2 * 4 * (128 + 2) * 4 + 1024 * 32
-    # 4 KV heads side by side, group 6 -> 6 heads per wave
-    assert ws_size(query_heads=24, kv_heads=4) == 1024 * 2 * 4 * 6 * (128 + 2) * 4 + 1024 * 32
+    # the streams read side by side x heads_per_wg rows of (D + 2) floats, plus two 16-byte
+    # records.  Streams side by side: gcd(streams, 12), halved while the batch holds fewer
+    # than 32 bands.  Group 4 -> 4 heads per wave; 2 KV heads, batch 2 -> 2 bands -> 1.
+    assert ws_size() == 1024 * 2 * 1 * 4 * (128 + 2) * 4 + 1024 * 32
+    # 32 sequences: 32 bands of 2 streams, kept side by side
+    assert ws_size(batch=32) == 1024 * 2 * 2 * 4 * (128 + 2) * 4 + 1024 * 32
+    # 4 KV heads (group 6 -> 6 heads per wave), batch 2: 4 side by side halved to 2
+    assert ws_size(query_heads=24, kv_heads=4) == 1024 * 2 * 2 * 6 * (128 + 2) * 4 + 1024 * 32
+    # batch 8 of 4 KV heads: 8 bands of 4 streams (fewer than 32) -> 16 bands of 2
+    assert ws_size(query_heads=24, kv_heads=4, batch=8) == 1024 * 2 * 2 * 6 * (128 + 2) * 4 + 1024 * 32
+    # batch 16 of 4 KV heads: 16 bands of 4 streams -> 2 side by side (32 bands would not be
+    # halved again); batch 32: 32 bands of 4, kept
+    assert ws_size(query_heads=24, kv_heads=4, batch=32) == 1024 * 2 * 4 * 6 * (128 + 2) * 4 + 1024 * 32
     # fixed partitions of one page -> 8 partitions of (D + 2) floats per (sequence, head)
     assert ws_size(partition_size=16) == 2 * 8 * 8 * (128 + 2) * 4
     assert ws_size(partition_size=16, max_context_length=40) == 2 * 8 * 3 * (128 + 2) * 4
