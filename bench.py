@@ -66,15 +66,39 @@ def parse():
     return ap.parse_args()
 
 
+def _code_only(text: str) -> str:
+    """C++ source with comments removed and whitespace runs collapsed (string and character
+    literals kept as they are), so that edits to comments leave the hash alone."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash() -> str:
-    """sha256 over the sources of the decode kernels and their launch code: counters taken
-    on other sources do not apply.  (pa_append.hip holds a separate kernel, not part of a
-    pa_decode call.)"""
+    """sha256 over the code (comments and whitespace aside) of the decode kernels and their
+    launch code: counters taken on other code do not apply.  (pa_append.hip holds a
+    separate kernel, not part of a pa_decode call.)"""
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
         if name.endswith((".hip", ".cpp", ".h")) and name != "pa_append.hip":
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+            with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+                h.update(name.encode() + b"\0" + _code_only(f.read()).encode())
     return h.hexdigest()
 
 

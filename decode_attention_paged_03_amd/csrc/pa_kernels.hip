@@ -5,9 +5,11 @@
 //  * Balanced (the default): a resident grid, one workgroup per CU, splits all token
 //    tiles of the batch evenly.  A sequence's streams (KV head, head chunk) are grouped in
 //    bands of `spw` streams that are read side by side: the waves of a workgroup take
-//    different streams of the same token range, so that every CU reads all row offsets
-//    of a page (the KV heads of a token sit next to each other) and the memory channels
-//    are loaded evenly.  Bands are laid end to end; workgroup w takes the units
+//    different streams of the same token range, so that a CU reads neighbouring row
+//    offsets of a page (the KV heads of a token sit next to each other) and the memory
+//    channels are loaded evenly.  (The plan halves spw when the batch holds few bands;
+//    each band then spans many workgroups and fewer rows per band make its merge
+//    cheaper.)  Bands are laid end to end; workgroup w takes the units
 //    [w N / W, (w+1) N / W) of the N (band, 16-token tile) units, and the waves reading
 //    one stream split that range in runs, the earlier rounds of waves taking somewhat
 //    more (they are issued first).  A stream that a wave holds entirely is
