@@ -1154,11 +1154,11 @@ pa_decode_balanced(DecodeArgs a) {
             float M = -INFINITY;
             float Ls = 0.f;
             float4_t o = {0.f, 0.f, 0.f, 0.f};
-            // Up to KF slots (two per wave, three waves per stream) are read all at once;
-            // empty slots inside the run fold in with weight 0, and lanes past the run's end
-            // re-read its first slot with weight 0.
-            constexpr int KF = 6;
-            if (s1 - s0 <= KF) {
+            // Runs of up to 6 or 12 slots (two per wave; three or six waves per stream) are
+            // read all at once; empty slots inside the run fold in with weight 0, and lanes
+            // past the run's end re-read its first slot with weight 0.
+            auto fold_slots = [&](auto kf) {
+                constexpr int KF = decltype(kf)::value;
                 float mk[KF], lk[KF];
                 float4_t ak[KF];
 #pragma unroll
@@ -1177,6 +1177,11 @@ pa_decode_balanced(DecodeArgs a) {
                     Ls += f * lk[k];
                     o += f * ak[k];
                 }
+            };
+            if (s1 - s0 <= 6) {
+                fold_slots(IntC<6>());
+            } else if (s1 - s0 <= 12) {
+                fold_slots(IntC<12>());
             } else {
                 for (int sl = s0; sl < s1; ++sl) {
                     M = fmaxf(M, s_m[sl][h]);
