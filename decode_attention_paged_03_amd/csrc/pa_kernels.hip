@@ -1235,12 +1235,11 @@ pa_decode_balanced(DecodeArgs a) {
 // pass.
 template <int D, int HP>
 __global__ void __launch_bounds__(kMergeThreads)
-pa_merge_balanced(DecodeArgs a, int n_wg) {
+pa_merge_balanced(DecodeArgs a) {
     constexpr int C4 = D / 4;
     constexpr int SC = kSliceCols;                  // float4 columns per task
     constexpr int NSL = C4 / SC;                    // tasks per row
     static_assert(C4 % SC == 0, "a row is a whole number of tasks");
-    (void)n_wg;
     const int x = blockIdx.x;
     const int tid = threadIdx.x;
     const int rows = a.spw * HP;
@@ -1518,7 +1517,7 @@ hipError_t launch_balanced_nw(const Plan& pl, const DecodeArgs& args, hipStream_
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NW * 64), lds, stream, args);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((pa_merge_balanced<D, HP>), dim3((unsigned)grid), dim3(kMergeThreads), 0, stream, args, grid);
+    hipLaunchKernelGGL((pa_merge_balanced<D, HP>), dim3((unsigned)grid), dim3(kMergeThreads), 0, stream, args);
     return hipGetLastError();
 }
 
