@@ -60,6 +60,9 @@ def parse():
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
                     help="turn a rocprofv3 --kernel-trace --stats output folder of this bench into "
                          "profiles/kernels_<workload>.txt")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="PMC_DIR",
+                    help="turn rocprofv3 --pmc output folders of the COUNTER_PASSES into "
+                         "profiles/counters_<workload>.txt")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc output folders (FETCH_SIZE, WRITE_SIZE) of "
                          "`bench.py --copy-calibration` into profiles/traffic_<workload>.txt")
@@ -160,6 +163,61 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str) -> str:
     lines.append(f"write_bytes_per_call: {write:.0f}")
     lines.append(f"traffic_bytes_per_call: {fetch + write:.0f}")
     path = os.path.join(PROFILES, f"traffic_{workload}.txt")
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return path
+
+
+# Counter passes for LDS, occupancy and MFMA figures (each within one pass's hardware
+# limits: at most 8 SQ and 2 GRBM counters).
+COUNTER_PASSES = (("SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_LDS", "SQ_WAVES",
+                   "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE"),
+                  ("MeanOccupancyPerActiveCU", "MfmaUtil"))
+
+
+def summarize_counters(folders, workload: str) -> str:
+    """Mean per dispatch of each counter of COUNTER_PASSES for the decode kernels, plus the
+    LDS bank-conflict rate (conflict cycles over conflict-free active LDS cycles, as
+    rocprofv3's LdsBankConflict)."""
+    names = [c for p in COUNTER_PASSES for c in p]
+    per = {}
+    for folder in folders:
+        for c in names:
+            try:
+                rows = _counter_rows(folder, c)
+            except SystemExit:
+                continue
+            for r in rows:
+                m = re.search(r"(pa_\w+)(<[^(]*>)?", r["Kernel_Name"])
+                if not m or m.group(1).startswith("pa_append"):
+                    continue
+                k = m.group(1) + (m.group(2) or "")
+                per.setdefault(k, {}).setdefault(c, []).append(float(r["Counter_Value"]))
+    if not per:
+        raise SystemExit(f"no decode-kernel counter values under {folders}")
+    lines = [f"# rocprofv3 counters of the decode kernels, workload {workload}",
+             f"kernel_source_sha256: {kernel_source_hash()}"]
+    for p in COUNTER_PASSES:
+        lines.append(f"command: rocprofv3 --pmc {' '.join(p)} --output-format csv -d <dir> -o run -- "
+                     f"python bench.py --workload {workload} --steps 10 --warmup 2 --no-cpu-baseline "
+                     "--append-steps 0")
+    lines.append("(mean per dispatch, warm-up dispatches included)")
+    for k, cs in per.items():
+        lines.append(f"{k}:")
+        for c in names:
+            if c in cs:
+                v = cs[c]
+                lines.append(f"  {c}: {sum(v) / len(v):.6g} (mean of {len(v)})")
+        bc = cs.get("SQ_LDS_BANK_CONFLICT")
+        act = cs.get("SQ_LDS_IDX_ACTIVE")
+        if bc and act and sum(act) > sum(bc):
+            lines.append(f"  lds_bank_conflict_rate: {sum(bc) / (sum(act) - sum(bc)):.4f} "
+                         "(conflict cycles per conflict-free active LDS cycle)")
+        w = cs.get("SQ_WAVES")
+        if w:
+            lines.append(f"  waves_per_dispatch: {sum(w) / len(w):.0f}")
+    path = os.path.join(PROFILES, f"counters_{workload}.txt")
     os.makedirs(PROFILES, exist_ok=True)
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -331,6 +389,9 @@ def main():
         return
     if args.summarize_pmc:
         print(summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload))
+        return
+    if args.summarize_counters:
+        print(summarize_counters(args.summarize_counters, args.workload))
         return
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "

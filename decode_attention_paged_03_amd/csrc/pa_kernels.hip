@@ -78,6 +78,12 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 // dword 3 of a raw buffer resource on this target, and the nontemporal cache policy bit
 constexpr int kBufferFlags = 0x00020000;
 constexpr int kLoadNontemporal = 2;
+// Row stride, in 16-byte chunks, of the whole-row K staging (16 chunks of data per row).
+// Measured with SQ_LDS_BANK_CONFLICT: 16 or 17 or 20 chunks leave the staging writes or
+// operand reads with bank conflicts (17: 0.66 M conflict cycles per call at 64 x 8 heads);
+// 18 chunks (288 bytes) has none.
+constexpr int kKtStride = 18;
+
 constexpr float kRescaleSlack = 8.0f;   // log2 units
 // byte offset that lies past every tile's buffer range (loads there return zero)
 constexpr uint32_t kOutOfRange = 0x7FFFFF00u;
@@ -278,9 +284,8 @@ struct WaveState {
 
     // One tile: tokens at or past n_valid are masked (n_valid in 1..16, wave-uniform).
     // With KROW, kb holds whole-row K chunks (see load_kv) and kt is this wave's LDS
-    // staging area of 16 slots x 17 16-byte chunks: slot m holds token pi(m) (the row
-    // stride of 17 chunks keeps both the writes and the operand reads free of bank
-    // conflicts); the score operands are read back in the MFMA layout.
+    // staging area of 16 slots x kKtStride 16-byte chunks: slot m holds token pi(m); the
+    // score operands are read back in the MFMA layout.
     template <bool KROW = false>
     __device__ __forceinline__ void tile(const uint4 (&qb)[G::UK], const uint4 (&kb)[G::UK],
                                          const uint32_t (&vb)[4][G::VW], int n_valid, float sl2,
@@ -292,11 +297,11 @@ struct WaveState {
             // these writes before the reads below (one wave; LDS executes in order)
             __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 #pragma unroll
-            for (int i = 0; i < 4; ++i) kt[(4 * L.g + i) * 17 + L.n] = kb[i];   // token 4 i + g = pi(4 g + i)
+            for (int i = 0; i < 4; ++i) kt[(4 * L.g + i) * kKtStride + L.n] = kb[i];   // token 4 i + g = pi(4 g + i)
             __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 #pragma unroll
             for (int j = 0; j < G::UK; ++j) {
-                const uint4 kj = kt[L.n * 17 + 4 * j + L.g];
+                const uint4 kj = kt[L.n * kKtStride + 4 * j + L.g];
                 s = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(kj), as_half8(qb[j]), s, 0, 0, 0);
             }
         } else {
@@ -809,7 +814,7 @@ pa_decode_balanced(DecodeArgs a) {
     __shared__ int s_meta[NS][3];    // stream id (-1: empty), first unit, end unit
     __shared__ int s_runs[NS + 1];   // first slot of each run of one stream's slots, then NS
     __shared__ int s_nruns;
-    __shared__ uint4 s_kt[KROW ? NW * 16 * 17 : 1];   // whole-row K staging, per wave
+    __shared__ uint4 s_kt[KROW ? NW * 16 * kKtStride : 1];   // whole-row K staging, per wave
 
     const int B = a.batch;
     int* s_pref = s_dyn;             // [B + 1]
@@ -863,7 +868,7 @@ pa_decode_balanced(DecodeArgs a) {
     const size_t page_bytes = tok_bytes << ps_log2;
     const uint32_t voff = (uint32_t)(L.g * tok_bytes) + 2u * G::E * L.n;
     const uint32_t koff = KROW ? voff : (uint32_t)(L.ktok * tok_bytes) + 16u * L.g;
-    uint4* const kt = KROW ? &s_kt[wave * 16 * 17] : nullptr;
+    uint4* const kt = KROW ? &s_kt[wave * 16 * kKtStride] : nullptr;
     const float sl2 = a.scale_log2;
 
     // Physical pages of the wave's units, 64 at a time: lane i holds the page of unit
@@ -1503,7 +1508,7 @@ template <int D, int HP, int NW, bool SPLIT>
 hipError_t launch_balanced_nw(const Plan& pl, const DecodeArgs& args, hipStream_t stream) {
     // Whole-row K loads (staged through LDS) were measured faster at every head count
     // (serving shape with 4 heads per wave: -1.1 us per call; long context, 6 heads:
-    // -0.7 us; mixed batch, 8 heads: -3 us).  Their 52 KB of staging is used when the
+    // -0.7 us; mixed batch, 8 heads: -3 us).  Their 55 KB of staging is used when the
     // kernel's LDS still fits next to the per-sequence arrays; otherwise K is loaded in
     // the MFMA layout.
     // (the staging is per wave: with 16 waves it would not fit next to the partial slots)
