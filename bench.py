@@ -173,13 +173,18 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str) -> str:
 # limits: at most 8 SQ and 2 GRBM counters).
 COUNTER_PASSES = (("SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_LDS", "SQ_WAVES",
                    "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE"),
-                  ("MeanOccupancyPerActiveCU", "MfmaUtil"))
+                  ("MeanOccupancyPerActiveCU", "MfmaUtil"),
+                  ("TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum", "TCC_EA0_RDREQ_64B_sum",
+                   "TCC_EA0_RDREQ_128B_sum"),
+                  ("TCC_HIT_sum", "TCC_MISS_sum", "TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum",
+                   "TCC_EA0_RDREQ_LEVEL_sum"))
 
 
 def summarize_counters(folders, workload: str) -> str:
     """Mean per dispatch of each counter of COUNTER_PASSES for the decode kernels, plus the
     LDS bank-conflict rate (conflict cycles over conflict-free active LDS cycles, as
-    rocprofv3's LdsBankConflict)."""
+    rocprofv3's LdsBankConflict), the share of HBM read requests that are whole 128-byte
+    lines, and the mean read latency by Little's law (queue level over requests)."""
     names = [c for p in COUNTER_PASSES for c in p]
     per = {}
     for folder in folders:
@@ -217,6 +222,13 @@ def summarize_counters(folders, workload: str) -> str:
         w = cs.get("SQ_WAVES")
         if w:
             lines.append(f"  waves_per_dispatch: {sum(w) / len(w):.0f}")
+        rq, r128 = cs.get("TCC_EA0_RDREQ_sum"), cs.get("TCC_EA0_RDREQ_128B_sum")
+        if rq and r128 and sum(rq) > 0:
+            lines.append(f"  hbm_read_requests_128B_fraction: {sum(r128) / sum(rq):.4f}")
+        lvl = cs.get("TCC_EA0_RDREQ_LEVEL_sum")
+        if rq and lvl and sum(rq) > 0:
+            lines.append(f"  mean_read_request_latency_l2_cycles: {sum(lvl) / sum(rq):.0f} "
+                         "(accumulated queue level over requests)")
     path = os.path.join(PROFILES, f"counters_{workload}.txt")
     os.makedirs(PROFILES, exist_ok=True)
     with open(path, "w") as f:
