@@ -78,6 +78,9 @@ SHAPES = [
     (24, 2, 64, 128, [129, 3000]),                              # G=12, page 128
     (12, 2, 128, 256, [256, 257, 2500]),                        # G=6, page 256
     (8, 2, 64, 16, [0, 37, 0, 100]),                            # empty sequences
+    (16, 16, 128, 16, [40, 900, 3000]),                         # 16 streams: spw 4 -> 2
+    (5, 5, 64, 16, [17, 1200, 2600, 5]),                         # 5 streams: bands of 1
+    (20, 10, 128, 32, [333, 4000]),                             # G=2, 10 streams: spw 2 -> 1
 ]
 
 
