@@ -177,7 +177,12 @@ COUNTER_PASSES = (("SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_LDS", 
                   ("TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum", "TCC_EA0_RDREQ_64B_sum",
                    "TCC_EA0_RDREQ_128B_sum"),
                   ("TCC_HIT_sum", "TCC_MISS_sum", "TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum",
-                   "TCC_EA0_RDREQ_LEVEL_sum"))
+                   "TCC_EA0_RDREQ_LEVEL_sum"),
+                  ("SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY",
+                   "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_VMEM", "SQ_ACTIVE_INST_LDS",
+                   "SQ_ACTIVE_INST_SCA"),
+                  ("SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_VMEM_RD", "SQ_INSTS_SMEM",
+                   "SQ_WAIT_INST_LDS", "SQ_ACTIVE_INST_MISC", "SQ_WAVES"))
 
 
 def summarize_counters(folders, workload: str) -> str:
@@ -222,6 +227,9 @@ def summarize_counters(folders, workload: str) -> str:
         w = cs.get("SQ_WAVES")
         if w:
             lines.append(f"  waves_per_dispatch: {sum(w) / len(w):.0f}")
+            for c in ("SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_VMEM_RD"):
+                if c in cs:
+                    lines.append(f"  {c.lower()}_per_wave: {sum(cs[c]) / len(cs[c]) / (sum(w) / len(w)):.0f}")
         rq, r128 = cs.get("TCC_EA0_RDREQ_sum"), cs.get("TCC_EA0_RDREQ_128B_sum")
         if rq and r128 and sum(rq) > 0:
             lines.append(f"  hbm_read_requests_128B_fraction: {sum(r128) / sum(rq):.4f}")
