@@ -758,6 +758,51 @@ __device__ __forceinline__ int tile_prefix(const int32_t* ctx, int B, int* s_pre
 
 // Position of unit t (0 <= t < N): sequence b (the smallest with SG * pref[b+1] > t),
 // band within the sequence, tile lt of the band.  The host keeps N below 2^31.
+// The sequence holding unit t, for a wave-uniform t: the number of sequences 1 .. B-1
+// whose first unit is at or before t (the prefix sums are non-decreasing), counted 64
+// entries per LDS read across the wave -- one read for up to 65 sequences, where a binary
+// search takes one dependent read per halving.  Large batches use the binary search.
+__device__ __forceinline__ int seq_of_unit_wave(int t, int B, int SG, const int* s_pref, int lane) {
+    if (B > 256) {
+        int lo = 0, hi = B - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (SG * s_pref[mid + 1] > t) hi = mid;
+            else lo = mid + 1;
+        }
+        return lo;
+    }
+    int b = 0;
+    for (int base = 1; base < B; base += 64) {
+        const int l = base + lane;
+        const bool at_or_before = l < B && SG * s_pref[l] <= t;
+        b += __popcll(__builtin_amdgcn_ballot_w64(at_or_before));
+    }
+    return b;
+}
+
+// The sequence holding unit t, given a sequence b0 at or before it (wave-uniform): the next
+// four sequence starts are read at once; only a unit more than four sequences past b0
+// falls back to a binary search.
+__device__ __forceinline__ int seq_of_unit_from(int t, int b0, int B, int SG, const int* s_pref) {
+    int c = 0;
+#pragma unroll
+    for (int k = 1; k <= 4; ++k) {
+        const int l = b0 + k;
+        c += (l < B && SG * s_pref[l] <= t) ? 1 : 0;
+    }
+    int lo = b0 + c;
+    if (c == 4) {
+        int hi = B - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (SG * s_pref[mid + 1] > t) hi = mid;
+            else lo = mid + 1;
+        }
+    }
+    return lo;
+}
+
 __device__ __forceinline__ void locate_unit(int t, int B, int SG, const int* s_pref, int& b, int& band, int& lt) {
     int lo = 0, hi = B - 1;
     while (lo < hi) {
@@ -874,11 +919,14 @@ pa_decode_balanced(DecodeArgs a) {
     // Physical pages of the wave's units, 64 at a time: lane i holds the page of unit
     // (wr0 + batch + i) (and, for pages of 8, the page of its second half).
     int btv = 0, btv2 = 0;
-    auto load_pages = [&](int batch) {
+    auto load_pages = [&](int batch, int b0) {
         const int t = wr0 + batch + L.lane;
         if (t < wr1) {
-            int b, band, lt;
-            locate_unit(t, B, SG, s_pref, b, band, lt);
+            // b0: the sequence of unit wr0 + batch (where the cursor stands)
+            const int b = seq_of_unit_from(t, b0, B, SG, s_pref);
+            const int Tb = s_pref[b + 1] - s_pref[b];
+            const int off = t - SG * s_pref[b];
+            const int lt = off - (off / Tb) * Tb;
             const int tok = lt * T;
             const int32_t* row = a.bt + (size_t)b * a.max_pages;
             btv = row[tok >> ps_log2];
@@ -905,14 +953,20 @@ pa_decode_balanced(DecodeArgs a) {
         cchunk = cs - ckvh * a.n_chunks;
     };
     if (nk > 0) {
-        locate_unit(wr0, B, SG, s_pref, cb, cband, cl);
+        cb = seq_of_unit_wave(wr0, B, SG, s_pref, L.lane);
+        {
+            const int Tb = s_pref[cb + 1] - s_pref[cb];
+            const int off = wr0 - SG * s_pref[cb];
+            cband = off / Tb;
+            cl = off - cband * Tb;
+        }
         cb = __builtin_amdgcn_readfirstlane(cb);
         cband = __builtin_amdgcn_readfirstlane(cband);
         cl = __builtin_amdgcn_readfirstlane(cl);
         cT = __builtin_amdgcn_readfirstlane(s_pref[cb + 1] - s_pref[cb]);
         cctx = __builtin_amdgcn_readfirstlane(s_ctx[cb]);
         set_stream();
-        load_pages(0);
+        load_pages(0, cb);
     }
     auto advance = [&]() {
         if (++cl == cT) {
@@ -933,7 +987,7 @@ pa_decode_balanced(DecodeArgs a) {
     // a segment, the segment's query rows come with it (into qr), so a new stream costs
     // no extra round trip.
     auto load_tile = [&](int i, Desc& d, uint4 (&kb)[G::UK], uint32_t (&vb)[4][G::VW], uint4 (&qr)[G::UK]) {
-        if ((i & 63) == 0 && i > 0) load_pages(i);
+        if ((i & 63) == 0 && i > 0) load_pages(i, cb);
         const int tok = cl * T;
         d.b = cb;
         d.s = cs;
