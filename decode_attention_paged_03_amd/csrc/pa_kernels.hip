@@ -1279,14 +1279,16 @@ pa_decode_balanced(DecodeArgs a) {
 // Merge of the balanced route.  Workgroup w of the decode kernel owns the band that
 // holds its last unit when that band starts in w and goes on past it (each crossing band
 // has exactly one owner); the pieces of stream sp, head h of such a band are rows
-// r(0) = ((w * 2 + side) * spw + sp) * HP + h and r(p) = r(0) + p * 2 * spw * HP rows
-// of side 0 of the following workgroups.  Merge block x reads workgroup x's two records
+// r(0) = ((w * 2 + side) * spw + sp) * HP + h of workgroup w and, for p >= 1,
+// r(p) = ((w + p) * 2 * spw + sp) * HP + h (side 0 of the following workgroups).  Merge
+// block x reads workgroup x's two records
 // (written by the decode kernel, no search here): the band it owns and the band that
 // covers its first unit.  A band spanning n workgroups has rows x (D / 32) tasks -- one
 // row, 128 bytes of columns -- and block o + j of its n blocks takes the j-th of n equal
 // shares, so the loads of every band are spread over all blocks it spans:
 //   * bands of at most kShortMerge pieces: one thread per (task, float4 column) loads all
-//     pieces at once; the block's shares of both its bands go in one pass;
+//     pieces at once; the block's shares of both its bands form one task list, taken 1, 2
+//     or 4 tasks per thread so that it usually needs one pass;
 //   * longer bands: the pieces of a task are split over groups of kLongUnroll, one group
 //     per thread, and the groups are combined through lane shuffles (and LDS when a task
 //     spans several waves).
