@@ -1,0 +1,65 @@
+"""Seeded random problem shapes through the default (balanced) route, against the oracle.
+
+Each case draws a batch size, a head layout (KV heads and group size, hence heads per wave
+and streams per sequence), a head dimension, a page size and a mix of context lengths
+(zeros, single tokens, a long sequence among short ones, runs of equal lengths), so that
+the split, the stream bands, the merge paths and the sequence search meet shapes no
+fixed list names.  The draws are seeded: every run checks the same cases.
+
+Bar: |gpu - oracle| <= 1e-3 * (1 + |oracle|), with NaN canaries never read.
+"""
+import numpy as np
+import pytest
+
+from decode_attention_paged_03_amd import pa
+from decode_attention_paged_03_amd import workloads as W
+
+import gpu_common as C
+
+pytestmark = pytest.mark.gpu
+
+N_CASES = 24
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    pa.load()
+    yield
+
+
+def _draw(seed):
+    rng = np.random.default_rng(seed)
+    kv_heads = int(rng.choice([1, 2, 3, 4, 8]))
+    group = int(rng.choice([1, 2, 3, 4, 5, 6, 8, 12, 16]))
+    head_dim = int(rng.choice([64, 128]))
+    page_size = int(rng.choice([8, 16, 32, 64, 128, 256]))
+    batch = int(rng.integers(1, 48))
+    kind = rng.integers(0, 4)
+    if kind == 0:                                   # uniform lengths
+        ctx = rng.integers(0, 3000, size=batch)
+    elif kind == 1:                                 # lognormal, clipped
+        ctx = np.clip(rng.lognormal(6.0, 1.2, size=batch), 1, 6000).astype(np.int64)
+    elif kind == 2:                                 # one long sequence among short ones
+        ctx = rng.integers(0, 40, size=batch)
+        ctx[rng.integers(0, batch)] = int(rng.integers(8000, 30000))
+    else:                                           # runs of equal lengths
+        ctx = np.repeat(rng.integers(1, 700, size=(batch + 3) // 4), 4)[:batch]
+    ctx[rng.random(batch) < 0.1] = 0                # some empty sequences
+    ctx[rng.random(batch) < 0.1] = 1                # some single tokens
+    # keep the oracle's work bounded (about 60 K tokens per case)
+    total = int(ctx.sum())
+    if total > 60000:
+        ctx = (ctx * (60000 / total)).astype(np.int64)
+    return dict(batch=batch, query_heads=kv_heads * group, kv_heads=kv_heads,
+                head_dim=head_dim, page_size=page_size, context_lengths=[int(c) for c in ctx])
+
+
+@pytest.mark.parametrize("case", range(N_CASES))
+def test_random_shape(case):
+    d = _draw(9900 + case)
+    wl = W.make_workload(name=f"random{case}", pool="holes10", seed=9950 + case, **d)
+    C.decode_and_check(wl, what=f"random case {case}: QH{d['query_heads']}/KVH{d['kv_heads']} "
+                                f"D{d['head_dim']} ps{d['page_size']} B{d['batch']}")
