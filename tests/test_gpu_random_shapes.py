@@ -63,3 +63,14 @@ def test_random_shape(case):
     wl = W.make_workload(name=f"random{case}", pool="holes10", seed=9950 + case, **d)
     C.decode_and_check(wl, what=f"random case {case}: QH{d['query_heads']}/KVH{d['kv_heads']} "
                                 f"D{d['head_dim']} ps{d['page_size']} B{d['batch']}")
+
+
+@pytest.mark.parametrize("case", range(0, N_CASES, 2))
+def test_random_shape_fixed_partitions(case):
+    """The same draws through the fixed-partition route, with a partition of 1, 2, 4 or 16
+    pages."""
+    d = _draw(9900 + case)
+    pages = [1, 2, 4, 16][case // 2 % 4]
+    wl = W.make_workload(name=f"random{case}", pool="holes10", seed=9950 + case, **d)
+    C.decode_and_check(wl, partition_size=pages * d["page_size"],
+                       what=f"random case {case}, partition of {pages} pages")
