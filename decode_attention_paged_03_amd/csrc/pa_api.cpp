@@ -4,6 +4,7 @@
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
+#include <string.h>
 
 #include <new>
 
@@ -116,29 +117,59 @@ int build_plan(const pa_problem* in, Plan* pl) {
         if ((long long)p.batch * (streams / out.spw) < kFewBands && out.spw % 2 == 0) out.spw /= 2;
         out.waves_per_stream = out.bal_waves / out.spw;
         out.bands = streams / out.spw;
-        // Rows of D floats (plus a (max, sum) pair each): per workgroup (up to
-        // kMaxBalancedWG), two sides x spw streams x heads_per_wg heads of piece
-        // triples; then two 16-byte merge records per workgroup.
         out.need_merge = true;
-        const size_t rows = (size_t)kMaxBalancedWG * 2 * out.spw * out.heads_per_wg;
-        out.ws_ml_offset = rows * (size_t)p.head_dim * sizeof(float);
-        out.ws_desc_offset = out.ws_ml_offset + rows * 2 * sizeof(float);
-        out.ws_bytes = out.ws_desc_offset + (size_t)kMaxBalancedWG * 2 * 16;
+        out.rows_per_wg = (size_t)2 * out.spw * out.heads_per_wg;
     } else {
         out.need_merge = out.force_split || out.n_part_max > 1;
-        if (out.need_merge) {
-            const size_t slots = (size_t)p.batch * p.query_heads * (size_t)out.n_part_max;
-            out.ws_ml_offset = slots * (size_t)p.head_dim * sizeof(float);
-            out.ws_bytes = out.ws_ml_offset + slots * 2 * sizeof(float);
-        }
     }
+    out.ws_bytes = workspace_layout(out, kMaxBalancedWG).bytes;
     *pl = out;
     return PA_OK;
+}
+
+WsLayout workspace_layout(const Plan& pl, int wg_slots) {
+    WsLayout l{0, 0, 0, wg_slots};
+    if (!pl.need_merge) return l;
+    size_t rows;
+    if (pl.balanced) {
+        // Rows of D floats (plus a (max, sum) pair each): per workgroup, two sides x spw
+        // streams x heads_per_wg heads of piece triples; then two 16-byte merge records
+        // per workgroup.
+        rows = (size_t)wg_slots * pl.rows_per_wg;
+    } else {
+        // one triple per (sequence, query head, partition)
+        rows = (size_t)pl.prob.batch * pl.prob.query_heads * (size_t)pl.n_part_max;
+    }
+    l.ml_offset = rows * (size_t)pl.prob.head_dim * sizeof(float);
+    l.desc_offset = l.ml_offset + rows * 2 * sizeof(float);
+    l.bytes = l.desc_offset + (pl.balanced ? (size_t)wg_slots * 2 * 16 : 0);
+    l.wg_slots = wg_slots;
+    return l;
 }
 
 }  // namespace pa
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// A float that is neither infinite nor NaN, tested on its bits (the library is built with
+// no-NaN arithmetic semantics, under which a library isfinite() may be folded away).
+static bool finite_bits(float x) {
+    uint32_t u;
+    memcpy(&u, &x, sizeof u);
+    return (u & 0x7f800000u) != 0x7f800000u;
+}
+
+// The checks pa_decode() and pa_decode_noalloc() share (host only).
+static pa_status check_decode_args(const pa_handle* handle, const void* query, const void* key_cache,
+                                   const void* value_cache, const int32_t* block_tables,
+                                   const int32_t* context_lengths, float scale, const float* out) {
+    if (!handle || !query || !key_cache || !value_cache || !block_tables || !context_lengths || !out)
+        return PA_ERR_INVALID_ARGUMENT;
+    if (!finite_bits(scale)) return PA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache) || !aligned16(out))
+        return PA_ERR_MISALIGNED;
+    return PA_OK;
+}
 
 extern "C" {
 
@@ -165,18 +196,42 @@ pa_status pa_decode(const pa_handle* handle, const void* query, const void* key_
                     const void* value_cache, const int32_t* block_tables,
                     const int32_t* context_lengths, float scale, float* out, void* workspace,
                     size_t workspace_bytes, hipStream_t stream) {
-    if (!handle || !query || !key_cache || !value_cache || !block_tables || !context_lengths || !out)
-        return PA_ERR_INVALID_ARGUMENT;
-    if (!isfinite(scale)) return PA_ERR_INVALID_ARGUMENT;
+    const pa_status st = check_decode_args(handle, query, key_cache, value_cache, block_tables,
+                                           context_lengths, scale, out);
+    if (st != PA_OK) return st;
     const pa::Plan& pl = handle->plan;
-    if (!aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache) || !aligned16(out))
-        return PA_ERR_MISALIGNED;
     if (pl.ws_bytes) {
         if (!workspace || workspace_bytes < pl.ws_bytes) return PA_ERR_WORKSPACE;
         if (!aligned16(workspace)) return PA_ERR_MISALIGNED;
     }
     hipError_t err = pa::launch(pl, query, key_cache, value_cache, block_tables, context_lengths,
-                                scale, out, workspace, stream);
+                                scale, out, workspace, pa::workspace_layout(pl, pa::kMaxBalancedWG),
+                                stream);
+    return err == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status pa_decode_noalloc(const pa_handle* handle, const void* query, const void* key_cache,
+                            const void* value_cache, const int32_t* block_tables,
+                            const int32_t* context_lengths, float scale, float* out,
+                            hipStream_t stream) {
+    const pa_status st = check_decode_args(handle, query, key_cache, value_cache, block_tables,
+                                           context_lengths, scale, out);
+    if (st != PA_OK) return st;
+    const pa::Plan& pl = handle->plan;
+    void* scratch = nullptr;
+    pa::WsLayout layout{0, 0, 0, 0};
+    if (pl.need_merge) {
+        // the balanced route's rows are indexed by workgroup: sized for this device's grid
+        const int slots = pl.balanced ? pa::device_compute_units() : 0;
+        if (pl.balanced && slots <= 0) return PA_ERR_HIP;
+        layout = pa::workspace_layout(pl, slots);
+        if (layout.bytes > pa::kNoallocScratchBytes) return PA_ERR_SCRATCH;
+        size_t cap = 0;
+        if (!pa::noalloc_scratch(&scratch, &cap)) return PA_ERR_HIP;
+        if (layout.bytes > cap) return PA_ERR_SCRATCH;
+    }
+    hipError_t err = pa::launch(pl, query, key_cache, value_cache, block_tables, context_lengths,
+                                scale, out, scratch, layout, stream);
     return err == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
@@ -217,6 +272,7 @@ const char* pa_status_string(int status) {
         case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE";
         case PA_ERR_HIP: return "PA_ERR_HIP";
         case PA_ERR_NO_MEMORY: return "PA_ERR_NO_MEMORY";
+        case PA_ERR_SCRATCH: return "PA_ERR_SCRATCH";
         default: return "PA_ERR_UNKNOWN";
     }
 }

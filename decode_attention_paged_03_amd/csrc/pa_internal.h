@@ -21,6 +21,11 @@ constexpr int kDefaultPartition = 1024;
 // workspace on the host, without asking the device).
 constexpr int kMaxBalancedBatch = 2048;
 constexpr int kMaxBalancedWG = 1024;
+// pa_decode_noalloc: bytes of the library's own device scratch array (per GPU).  Enough for
+// the balanced route of every supported shape on a part with up to 320 compute units
+// (2 sides x 12 streams x 8 heads of 520-byte rows per workgroup, plus its records), and for
+// fixed partitions up to that size.
+constexpr size_t kNoallocScratchBytes = (size_t)PA_NOALLOC_SCRATCH_BYTES;
 // Query heads one wave scores at once (MFMA rows are 16; LDS partial slots are sized
 // for this many heads).
 constexpr int kMaxHeadsPerWave = 8;
@@ -42,20 +47,38 @@ struct Plan {
     // both
     int ps_log2;            // log2(page_size)
     bool need_merge;        // a merge kernel is launched
-    size_t ws_bytes;        // workspace bytes (0 when need_merge is false)
-    size_t ws_ml_offset;    // byte offset of the (max, sum) pairs inside the workspace
-    size_t ws_desc_offset;  // balanced route: byte offset of the per-workgroup merge records
+    size_t rows_per_wg;     // balanced route: partial rows per workgroup (2 sides x spw x heads)
+    size_t ws_bytes;        // workspace bytes pa_workspace_size() reports (0 when need_merge is
+                            // false): the layout for kMaxBalancedWG workgroups
     long long decode_grid;  // workgroups of the fixed-partition decode kernel
     long long merge_grid;   // workgroups of the fixed-partition merge kernel
 };
 
+// Where the parts of the workspace start.  The balanced route's partial rows are indexed
+// by workgroup, so its layout depends on how many workgroups it is sized for: the
+// caller-provided workspace is sized for kMaxBalancedWG (no device query on the host), the
+// library's own scratch (pa_decode_noalloc) for the device's compute units.
+struct WsLayout {
+    size_t ml_offset;       // byte offset of the (max, sum) pairs
+    size_t desc_offset;     // balanced route: byte offset of the per-workgroup merge records
+    size_t bytes;           // total (0 when no merge is launched)
+    int wg_slots;           // balanced route: workgroups the partial rows are sized for
+};
+WsLayout workspace_layout(const Plan& plan, int wg_slots);
+
 // Host-only validation + planning; returns a pa_status.
 int build_plan(const pa_problem* p, Plan* out);
 
-// Enqueue the decode (and, if planned, merge) kernels.  Pointers already validated.
+// Compute units of the current device (capped at kMaxBalancedWG), queried once per device
+// and cached; 0 when the HIP runtime reports an error.
+int device_compute_units();
+
+// Enqueue the decode (and, if planned, merge) kernels.  Pointers already validated; the
+// workspace holds at least layout.bytes bytes laid out as `layout`, and the balanced route's
+// grid (the device's compute units) is at most the workgroups the layout is sized for.
 hipError_t launch(const Plan& plan, const void* q, const void* k, const void* v,
                   const int32_t* block_tables, const int32_t* ctx, float scale, float* out,
-                  void* workspace, hipStream_t stream);
+                  void* workspace, const WsLayout& layout, hipStream_t stream);
 
 // pa_append: workgroup size for a sequence's kv_heads * head_dim / 8 16-byte chunks (whole
 // waves, at most kAppendThreads; more chunks take more workgroups along grid y).
@@ -63,6 +86,12 @@ constexpr int kAppendThreads = 256;
 inline int append_threads(long long row_chunks) {
     return row_chunks >= kAppendThreads ? kAppendThreads : (int)((row_chunks + 63) / 64 * 64);
 }
+
+// pa_decode_noalloc: the library's own scratch array on the current device.  The first
+// call on a device looks up the array's device address (and the device's compute units);
+// later calls return the cached values.  Returns false when the HIP runtime reports an
+// error.
+bool noalloc_scratch(void** ptr, size_t* bytes);
 
 // Enqueue the kernel that stores one new key / value row per sequence (pa_append).
 hipError_t launch_append(const Plan& plan, const void* new_k, const void* new_v, void* k_cache,

@@ -61,6 +61,8 @@
 
 #include <math.h>
 
+#include <atomic>
+
 #include "pa_internal.h"
 
 namespace pa {
@@ -1540,14 +1542,7 @@ constexpr int kWaves = PA_WAVES;
 constexpr int kDepth = PA_DEPTH;
 constexpr int kBalDepth = PA_BAL_DEPTH;
 
-// Compute units of the current device, capped at kMaxBalancedWG.  Host-side queries
-// only; nothing is enqueued.
-int balanced_grid() {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    return cus < kMaxBalancedWG ? cus : kMaxBalancedWG;
-}
+int balanced_grid() { return device_compute_units(); }
 
 // LDS a gfx950 workgroup may use (the CU's 160 KB).
 constexpr size_t kLdsPerWorkgroup = 160 * 1024;
@@ -1561,7 +1556,7 @@ size_t static_lds_bytes(K kern) {
 }
 
 template <int D, int HP, int NW, bool SPLIT>
-hipError_t launch_balanced_nw(const Plan& pl, const DecodeArgs& args, hipStream_t stream) {
+hipError_t launch_balanced_nw(const Plan& pl, const DecodeArgs& args, int ws_slots, hipStream_t stream) {
     // Whole-row K loads (staged through LDS) were measured faster at every head count
     // (serving shape with 4 heads per wave: -1.1 us per call; long context, 6 heads:
     // -0.7 us; mixed batch, 8 heads: -3 us).  Their 55 KB of staging is used when the
@@ -1575,6 +1570,7 @@ hipError_t launch_balanced_nw(const Plan& pl, const DecodeArgs& args, hipStream_
     const auto kern = (row_static != SIZE_MAX && row_static + lds <= kLdsPerWorkgroup) ? kern_row : kern_mfma;
     const int grid = balanced_grid();
     if (grid <= 0) return hipErrorInvalidDevice;
+    if (grid > ws_slots) return hipErrorInvalidValue;   // the workspace holds fewer workgroups' rows
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NW * 64), lds, stream, args);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
@@ -1583,22 +1579,23 @@ hipError_t launch_balanced_nw(const Plan& pl, const DecodeArgs& args, hipStream_
 }
 
 template <int D, int HP, bool SPLIT>
-hipError_t launch_balanced(const Plan& pl, const DecodeArgs& args, hipStream_t stream) {
+hipError_t launch_balanced(const Plan& pl, const DecodeArgs& args, int ws_slots, hipStream_t stream) {
     switch (pl.bal_waves) {
-        case 12: return launch_balanced_nw<D, HP, 12, SPLIT>(pl, args, stream);
+        case 12: return launch_balanced_nw<D, HP, 12, SPLIT>(pl, args, ws_slots, stream);
 #ifdef PA_BAL_WAVES
-        case 8: return launch_balanced_nw<D, HP, 8, SPLIT>(pl, args, stream);
-        case 16: return launch_balanced_nw<D, HP, 16, SPLIT>(pl, args, stream);
+        case 8: return launch_balanced_nw<D, HP, 8, SPLIT>(pl, args, ws_slots, stream);
+        case 16: return launch_balanced_nw<D, HP, 16, SPLIT>(pl, args, ws_slots, stream);
 #endif
         default: return hipErrorInvalidValue;
     }
 }
 
 template <int D, int HP>
-hipError_t launch_decode(const Plan& pl, const DecodeArgs& args, hipStream_t stream) {
+hipError_t launch_decode(const Plan& pl, const DecodeArgs& args, int ws_slots, hipStream_t stream) {
     const bool split = pl.prob.page_size < 16;
     if (pl.balanced)
-        return split ? launch_balanced<D, HP, true>(pl, args, stream) : launch_balanced<D, HP, false>(pl, args, stream);
+        return split ? launch_balanced<D, HP, true>(pl, args, ws_slots, stream)
+                     : launch_balanced<D, HP, false>(pl, args, ws_slots, stream);
     if (!split)
         hipLaunchKernelGGL((pa_decode_kernel<D, HP, kDepth, kWaves, false>),
                            dim3((unsigned)pl.decode_grid), dim3(kWaves * 64), 0, stream, args);
@@ -1609,34 +1606,54 @@ hipError_t launch_decode(const Plan& pl, const DecodeArgs& args, hipStream_t str
 }
 
 template <int D>
-hipError_t launch_decode_d(const Plan& pl, const DecodeArgs& args, hipStream_t stream) {
+hipError_t launch_decode_d(const Plan& pl, const DecodeArgs& args, int ws_slots, hipStream_t stream) {
     static_assert(kMaxHeadsPerWave == 8, "instantiations below cover 1..8 heads");
     switch (pl.heads_per_wg) {
-        case 1: return launch_decode<D, 1>(pl, args, stream);
-        case 2: return launch_decode<D, 2>(pl, args, stream);
-        case 3: return launch_decode<D, 3>(pl, args, stream);
-        case 4: return launch_decode<D, 4>(pl, args, stream);
-        case 5: return launch_decode<D, 5>(pl, args, stream);
-        case 6: return launch_decode<D, 6>(pl, args, stream);
-        case 7: return launch_decode<D, 7>(pl, args, stream);
-        case 8: return launch_decode<D, 8>(pl, args, stream);
+        case 1: return launch_decode<D, 1>(pl, args, ws_slots, stream);
+        case 2: return launch_decode<D, 2>(pl, args, ws_slots, stream);
+        case 3: return launch_decode<D, 3>(pl, args, ws_slots, stream);
+        case 4: return launch_decode<D, 4>(pl, args, ws_slots, stream);
+        case 5: return launch_decode<D, 5>(pl, args, ws_slots, stream);
+        case 6: return launch_decode<D, 6>(pl, args, ws_slots, stream);
+        case 7: return launch_decode<D, 7>(pl, args, ws_slots, stream);
+        case 8: return launch_decode<D, 8>(pl, args, ws_slots, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
 }  // namespace
 
+namespace {
+constexpr int kMaxDevices = 256;
+std::atomic<int> g_cus[kMaxDevices];   // 0: not asked yet
+}  // namespace
+
+int device_compute_units() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+    if (dev < kMaxDevices) {
+        const int c = g_cus[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        return 0;
+    cus = cus < kMaxBalancedWG ? cus : kMaxBalancedWG;
+    if (dev < kMaxDevices) g_cus[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
+
 hipError_t launch(const Plan& pl, const void* q, const void* k, const void* v,
                   const int32_t* block_tables, const int32_t* ctx, float scale, float* out,
-                  void* workspace, hipStream_t stream) {
+                  void* workspace, const WsLayout& layout, hipStream_t stream) {
     const pa_problem& p = pl.prob;
     float* ws_acc = nullptr;
     float* ws_ml = nullptr;
     int4* ws_desc = nullptr;
     if (pl.need_merge) {
         ws_acc = static_cast<float*>(workspace);
-        ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.ws_ml_offset);
-        if (pl.balanced) ws_desc = reinterpret_cast<int4*>(static_cast<char*>(workspace) + pl.ws_desc_offset);
+        ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + layout.ml_offset);
+        if (pl.balanced) ws_desc = reinterpret_cast<int4*>(static_cast<char*>(workspace) + layout.desc_offset);
     }
     DecodeArgs da;
     da.q = static_cast<const _Float16*>(q);
@@ -1664,8 +1681,8 @@ hipError_t launch(const Plan& pl, const void* q, const void* k, const void* v,
     da.waves_per_stream = pl.waves_per_stream;
     da.bands = pl.bands;
 
-    hipError_t err = (p.head_dim == 128) ? launch_decode_d<128>(pl, da, stream)
-                                         : launch_decode_d<64>(pl, da, stream);
+    hipError_t err = (p.head_dim == 128) ? launch_decode_d<128>(pl, da, layout.wg_slots, stream)
+                                         : launch_decode_d<64>(pl, da, layout.wg_slots, stream);
     if (err != hipSuccess || pl.balanced || !pl.need_merge) return err;
 
     MergeArgs ma;

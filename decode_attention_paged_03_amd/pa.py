@@ -1,10 +1,10 @@
 """ctypes binding of libpa.so -- argument marshalling only.
 
 The functions below carry the C ABI's names (``pa_create``, ``pa_workspace_size``,
-``pa_decode``, ``pa_append``, ``pa_destroy``, ``pa_status_string``) and take plain integers for
-device pointers and the stream.  ``PagedDecoder`` is a convenience wrapper that
-takes torch tensors, checks their dtype / device / contiguity and passes their
-``data_ptr()`` through; every step of the computation runs in the library's HIP
+``pa_decode``, ``pa_decode_noalloc``, ``pa_append``, ``pa_destroy``, ``pa_status_string``) and
+take plain integers for device pointers and the stream.  ``PagedDecoder`` is a
+convenience wrapper that takes torch tensors, checks their dtype / device / contiguity
+and passes their ``data_ptr()`` through; every step of the computation runs in the library's HIP
 kernels.  There is no fallback: if ``libpa.so`` is missing, ``load()`` raises.
 """
 from __future__ import annotations
@@ -23,12 +23,15 @@ PA_ERR_MISALIGNED = 3
 PA_ERR_WORKSPACE = 4
 PA_ERR_HIP = 5
 PA_ERR_NO_MEMORY = 6
+PA_ERR_SCRATCH = 7
+
+PA_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 PA_FLAG_FORCE_SPLIT = 0x1
 PA_FLAG_FORCE_SINGLE = 0x2
 
-EXPORTED = ("pa_create", "pa_workspace_size", "pa_decode", "pa_append", "pa_destroy",
-            "pa_status_string")
+EXPORTED = ("pa_create", "pa_workspace_size", "pa_decode", "pa_decode_noalloc", "pa_append",
+            "pa_destroy", "pa_status_string")
 
 
 class pa_problem(ctypes.Structure):
@@ -64,6 +67,8 @@ def load() -> ctypes.CDLL:
     lib.pa_workspace_size.restype = ctypes.c_int
     lib.pa_decode.argtypes = [P, P, P, P, P, P, ctypes.c_float, P, P, ctypes.c_size_t, P]
     lib.pa_decode.restype = ctypes.c_int
+    lib.pa_decode_noalloc.argtypes = [P, P, P, P, P, P, ctypes.c_float, P, P]
+    lib.pa_decode_noalloc.restype = ctypes.c_int
     lib.pa_append.argtypes = [P, P, P, P, P, P, P, P]
     lib.pa_append.restype = ctypes.c_int
     lib.pa_destroy.argtypes = [P]
@@ -101,6 +106,14 @@ def pa_decode(handle, query: int, key_cache: int, value_cache: int, block_tables
                           float(scale), out, workspace or None, int(workspace_bytes), stream or None)
     if st != PA_OK:
         raise PaError(st, "pa_decode")
+
+
+def pa_decode_noalloc(handle, query: int, key_cache: int, value_cache: int, block_tables: int,
+                      context_lengths: int, scale: float, out: int, stream: int) -> None:
+    st = load().pa_decode_noalloc(handle, query, key_cache, value_cache, block_tables,
+                                  context_lengths, float(scale), out, stream or None)
+    if st != PA_OK:
+        raise PaError(st, "pa_decode_noalloc")
 
 
 def pa_append(handle, new_key: int, new_value: int, key_cache: int, value_cache: int,

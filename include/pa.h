@@ -59,8 +59,14 @@ typedef enum pa_status {
                                     aligned                                                     */
     PA_ERR_WORKSPACE = 4,        /* workspace missing or smaller than pa_workspace_size()        */
     PA_ERR_HIP = 5,              /* the HIP runtime reported an error on launch                  */
-    PA_ERR_NO_MEMORY = 6         /* host allocation of the handle failed                         */
+    PA_ERR_NO_MEMORY = 6,        /* host allocation of the handle failed                         */
+    PA_ERR_SCRATCH = 7           /* pa_decode_noalloc: the problem needs more workspace than the
+                                    library's scratch array holds (PA_NOALLOC_SCRATCH_BYTES)      */
 } pa_status;
+
+/* Bytes of the device scratch array pa_decode_noalloc() uses in place of a workspace (one
+ * array per GPU, held until the process ends). */
+#define PA_NOALLOC_SCRATCH_BYTES (32u << 20)
 
 /* Flags for pa_problem.flags */
 #define PA_FLAG_FORCE_SPLIT  0x1u /* route every sequence through partition triples + merge */
@@ -111,6 +117,24 @@ pa_status pa_decode(const pa_handle *handle, const void *query, const void *key_
                     const void *value_cache, const int32_t *block_tables,
                     const int32_t *context_lengths, float scale, float *out, void *workspace,
                     size_t workspace_bytes, hipStream_t stream);
+
+/* pa_decode() for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  It takes pa_decode()'s
+ * arguments except the workspace, and uses instead a device array inside the library of
+ * PA_NOALLOC_SCRATCH_BYTES (32 MiB) per GPU, which each GPU holds until the process ends.
+ * The first call on a device (with that device current) looks up the array's address and
+ * the device's compute-unit count and caches both; no call allocates (no hipMalloc,
+ * hipFree or allocating library routine), copies to or from the host or synchronises.
+ * Returns PA_ERR_SCRATCH, before enqueuing anything, when the problem needs more workspace
+ * than the array holds (e.g. fixed partitions over a large batch; the default route of
+ * every supported shape fits on a GPU of up to 320 compute units).
+ * All calls on one GPU share its array, and the array keeps the last call's contents: two
+ * calls that may run at the same time on one GPU (two streams, two threads without
+ * ordering) race and corrupt each other's results.  Order them on one stream. */
+pa_status pa_decode_noalloc(const pa_handle *handle, const void *query, const void *key_cache,
+                            const void *value_cache, const int32_t *block_tables,
+                            const int32_t *context_lengths, float scale, float *out,
+                            hipStream_t stream);
 
 /* Enqueue the step before a decode: store one new token's key and value rows per
  * sequence in the paged cache.  The cache exists so that earlier tokens' keys and values

@@ -151,6 +151,37 @@ def test_decode_rejects_before_any_hip_call(lib):
         pa.pa_destroy(h)
 
 
+def test_decode_noalloc_rejects_before_any_hip_call(lib):
+    """pa_decode_noalloc checks what pa_decode checks, and refuses a fixed-partition problem
+    whose workspace passes the library's scratch array before touching the device (the
+    balanced route's size depends on the device's compute units, so its check needs one)."""
+    big = pa.pa_create(good(batch=64, query_heads=32, kv_heads=8, max_pages_per_sequence=128,
+                            num_physical_pages=8192, partition_size=16))
+    small = pa.pa_create(good(partition_size=16))
+    A = 0x10000          # aligned fake device addresses: never dereferenced on these paths
+    try:
+        assert pa.pa_workspace_size(big) > pa.PA_NOALLOC_SCRATCH_BYTES
+        assert lib.pa_decode_noalloc(big, A, A, A, A, A, 0.1, A, None) == pa.PA_ERR_SCRATCH
+        names = ("query", "key_cache", "value_cache", "block_tables", "context_lengths", "out")
+
+        def status(scale=0.1, **over):
+            a = dict.fromkeys(names, A)
+            a.update(over)
+            return lib.pa_decode_noalloc(small, a["query"], a["key_cache"], a["value_cache"],
+                                         a["block_tables"], a["context_lengths"], scale,
+                                         a["out"], None)
+        for name in names:
+            assert status(**{name: None}) == pa.PA_ERR_INVALID_ARGUMENT, name
+        for name in ("query", "key_cache", "value_cache", "out"):
+            assert status(**{name: A + 8}) == pa.PA_ERR_MISALIGNED, name
+        assert status(scale=float("nan")) == pa.PA_ERR_INVALID_ARGUMENT
+        assert status(scale=float("-inf")) == pa.PA_ERR_INVALID_ARGUMENT
+        assert lib.pa_decode_noalloc(None, A, A, A, A, A, 0.1, A, None) == pa.PA_ERR_INVALID_ARGUMENT
+    finally:
+        pa.pa_destroy(big)
+        pa.pa_destroy(small)
+
+
 def test_append_rejects_before_any_hip_call(lib):
     h = pa.pa_create(good())
     A = 0x10000          # aligned fake device addresses: never dereferenced on these paths
@@ -172,7 +203,7 @@ def test_append_rejects_before_any_hip_call(lib):
 
 def test_status_strings(lib):
     names = ["PA_OK", "PA_ERR_INVALID_ARGUMENT", "PA_ERR_UNSUPPORTED", "PA_ERR_MISALIGNED",
-             "PA_ERR_WORKSPACE", "PA_ERR_HIP", "PA_ERR_NO_MEMORY"]
+             "PA_ERR_WORKSPACE", "PA_ERR_HIP", "PA_ERR_NO_MEMORY", "PA_ERR_SCRATCH"]
     for i, n in enumerate(names):
         assert pa.pa_status_string(i) == n
     assert pa.pa_status_string(99) == "PA_ERR_UNKNOWN"

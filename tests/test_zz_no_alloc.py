@@ -1,0 +1,107 @@
+"""pa_decode_noalloc: the decode step with the library's own device scratch array in place
+of a caller workspace.  Its output must equal pa_decode's (same kernels, same split) on
+two calls in a row, the second over a smaller input while the array still holds the
+first call's partial results; both are also checked against the fp64 oracle, with the
+parity bar |gpu - oracle| <= 1e-3 * (1 + |oracle|)."""
+import numpy as np
+import pytest
+
+from decode_attention_paged_03_amd import pa
+from decode_attention_paged_03_amd import workloads as W
+
+import gpu_common as C
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    pa.load()
+    yield
+
+
+def _noalloc(dec, dev, out):
+    wl = dev.wl
+    pa.pa_decode_noalloc(dec.handle, dev.q.data_ptr(), dev.k.data_ptr(), dev.v.data_ptr(),
+                         dev.bt.data_ptr(), dev.ctx.data_ptr(), wl.scale, out.data_ptr(),
+                         0)
+
+
+@pytest.mark.parametrize("route", ["balanced", "fixed256"])
+def test_noalloc_two_calls_match_pa_decode(route):
+    """batch64, then small_batch (a smaller batch with fewer pieces), back to back on one
+    stream through pa_decode_noalloc; each equals pa_decode with a caller workspace bit for
+    bit and is within the parity bar of the oracle."""
+    import torch
+    part = 0 if route == "balanced" else 256
+    cases = [W.make_named("batch64"), W.make_named("small_batch")]
+    devs, decs, refs, outs = [], [], [], []
+    try:
+        for wl in cases:
+            C.say(f"[case] noalloc {route}: {wl.summary()}")
+            dev = C.Device(wl)
+            dec = pa.decoder_for(wl, partition_size=part)
+            devs.append(dev)
+            decs.append(dec)
+            refs.append(dev.run(dec).clone())           # pa_decode, caller workspace
+            outs.append(torch.full_like(refs[-1], float("nan")))
+        torch.cuda.synchronize()
+        for dec, dev, out in zip(decs, devs, outs):      # two calls in a row
+            _noalloc(dec, dev, out)
+        torch.cuda.synchronize()
+        for wl, ref, out in zip(cases, refs, outs):
+            assert torch.equal(ref.view(torch.int32), out.view(torch.int32)), \
+                f"{wl.name}: pa_decode_noalloc differs from pa_decode"
+            C.check_against_oracle(out.cpu().numpy(),
+                                   C.oracle.attend_workload(wl, nthreads=C.oracle_threads()),
+                                   f"noalloc {route} {wl.name}")
+    finally:
+        for dec in decs:
+            dec.close()
+
+
+def test_noalloc_repeat_after_smaller_call():
+    """The array keeps the last call's contents: a long-context call after a short one, and
+    the short one again, still equal pa_decode bit for bit."""
+    import torch
+    order = [W.make_named("tiny"), W.make_named("long100k"), W.make_named("tiny")]
+    for wl in order:
+        C.say(f"[case] noalloc sequence: {wl.summary()}")
+        dev = C.Device(wl)
+        dec = pa.decoder_for(wl, partition_size=0)
+        try:
+            ref = dev.run(dec).clone()
+            out = torch.full_like(ref, float("nan"))
+            _noalloc(dec, dev, out)
+            torch.cuda.synchronize()
+            assert torch.equal(ref.view(torch.int32), out.view(torch.int32)), wl.name
+        finally:
+            dec.close()
+
+
+def test_noalloc_rejects_oversized_problem():
+    """A problem whose workspace passes the array's size is refused before anything is
+    enqueued: the output buffer is left as it was."""
+    import torch
+    prob = pa.make_problem(batch=64, query_heads=32, kv_heads=8, head_dim=128, page_size=16,
+                           max_pages_per_sequence=128, num_physical_pages=8192,
+                           partition_size=16)
+    h = pa.pa_create(prob)
+    try:
+        assert pa.pa_workspace_size(h) > pa.PA_NOALLOC_SCRATCH_BYTES
+        q = torch.zeros((64, 32, 128), dtype=torch.float16, device="cuda")
+        kv = torch.zeros((8, 16, 8, 128), dtype=torch.float16, device="cuda")
+        bt = torch.zeros((64, 128), dtype=torch.int32, device="cuda")
+        ctx = torch.ones(64, dtype=torch.int32, device="cuda")
+        out = torch.full((64, 32, 128), 7.0, dtype=torch.float32, device="cuda")
+        with pytest.raises(pa.PaError) as e:
+            pa.pa_decode_noalloc(h, q.data_ptr(), kv.data_ptr(), kv.data_ptr(), bt.data_ptr(),
+                                 ctx.data_ptr(), 0.1, out.data_ptr(), 0)
+        assert e.value.status == pa.PA_ERR_SCRATCH
+        torch.cuda.synchronize()
+        assert bool((out == 7.0).all())
+    finally:
+        pa.pa_destroy(h)
