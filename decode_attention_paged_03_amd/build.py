@@ -62,6 +62,49 @@ def build(verbose: bool = False, asm_dir: str | None = None, defines=(), out: st
     return out
 
 
+_FIELDS = (("TotalSGPRs", "sgpr"), ("VGPRs", "vgpr"), ("AGPRs", "agpr"),
+           ("ScratchSize [bytes/lane]", "scratch"), ("Occupancy [waves/SIMD]", "waves/simd"),
+           ("SGPRs Spill", "sgpr_spill"), ("VGPRs Spill", "vgpr_spill"),
+           ("LDS Size [bytes/block]", "lds"))
+
+
+def parse_resource_usage(text: str) -> dict:
+    """{mangled kernel name: {field: int}} from clang's -Rpass-analysis=kernel-resource-usage
+    remarks."""
+    import re
+    out, cur = {}, None
+    for line in text.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            cur = out.setdefault(m.group(1), {})
+            continue
+        m = re.search(r"remark:\s+([A-Za-z][A-Za-z /\[\]]*?): (\d+) \[", line)
+        if m and cur is not None:
+            for name, key in _FIELDS:
+                if m.group(1) == name:
+                    cur[key] = int(m.group(2))
+    return out
+
+
+def resource_table(text: str) -> str:
+    """One line per kernel: registers, scratch, occupancy and LDS."""
+    import re
+    rows = []
+    for name, f in parse_resource_usage(text).items():
+        m = re.search(r"(pa_\w+?)(I.*)?E?vNS0_|(pa_\w+)", name)
+        short = name
+        dm = re.search(r"N_1\d+(pa_[a-z_]+)(I[^E]*(?:E[^v]*)?)?", name)
+        if dm:
+            short = dm.group(1) + "<" + ",".join(re.findall(r"Li(\d+)E|Lb(\d)E", name and dm.group(2) or "") and
+                                               [a or b for a, b in re.findall(r"Li(\d+)E|Lb(\d)E", dm.group(2) or "")]) + ">"
+        rows.append((short, f))
+    cols = [key for _, key in _FIELDS]
+    lines = [f"{'kernel':<40} " + " ".join(f"{c:>10}" for c in cols)]
+    for short, f in sorted(rows):
+        lines.append(f"{short:<40} " + " ".join(f"{f.get(c, -1):>10}" for c in cols))
+    return "\n".join(lines)
+
+
 if __name__ == "__main__":
     asm = None
     if "--asm" in sys.argv:

@@ -45,15 +45,17 @@
 //   softmax the reference max of a head only moves (and the accumulators are rescaled)
 //           when a score exceeds it by more than kRescaleSlack (2^8), so in steady state
 //           a tile costs one exp2 per score and no reduction.  Any reference value gives
-//           the same ratio acc / l; the slack only bounds the weights (<= 256, exact
-//           range for fp16).
-//   P.V     with v_mfma_f32_16x16x16_f16: A = the weights rounded to fp16 -- already in
-//           the A layout (lane (n, g) holds head n, tokens g + 4i) -- and B = V.  Lane
-//           (n, g) loads dims E n .. E n + E - 1 (E = D / 16) of rows g, g + 4, g + 8,
-//           g + 12 with one wide load per row (a load instruction covers four whole rows),
-//           and v_perm regroups them into four tokens of one dim; MFMA c takes dims
-//           E n + c.  The weight sum l adds the same rounded weights, so the output is an
-//           exact convex combination of V rows.  Lane (n, g) ends up holding head 4g + i
+//           the same ratio acc / l; the slack only bounds the weights (<= 256, inside
+//           fp16's range).
+//   P.V     with v_mfma_f32_16x16x32_f16: A = each weight as two fp16 terms, p_hi =
+//           fp16(p) and p_lo = fp16(p - p_hi) -- the score layout already is the A
+//           layout (lane (n, g) holds head n, tokens g + 4i) -- and B = the same four V
+//           rows twice, once against each term.  Lane (n, g) loads dims E n .. E n + E - 1
+//           (E = D / 16) of rows g, g + 4, g + 8, g + 12 with one wide load per row (a load
+//           instruction covers four whole rows), and v_perm regroups them into four tokens
+//           of one dim; MFMA c takes dims E n + c.  The weight sum l adds the same
+//           p_hi + p_lo, so the output is a convex combination of V rows with weights
+//           within about 2^-23 of exact.  Lane (n, g) ends up holding head 4g + i
 //           (register i), dims E n .. E n + E - 1.
 // The next tile's loads (nontemporal) are issued before a tile is consumed when the
 // route prefetches.
@@ -68,7 +70,6 @@
 namespace pa {
 namespace {
 
-typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
@@ -336,21 +337,31 @@ struct WaveState {
                 for (int c = 0; c < G::E; ++c) acc[c][i] *= ai;
             }
         }
-        half4_t p;
+        // Weights in two fp16 terms: p_hi = fp16(p), p_lo = fp16(p - p_hi) (about 22 bits of
+        // p; a single fp16 rounding would cost up to 2^-12 of each weight, an error that
+        // grows with the spread of the value rows).  A operand of the 16x16x32 product:
+        // k = 8 g + i holds p_hi of token g + 4 i, k = 8 g + 4 + i its p_lo.
+        half8_t pw;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            p[i] = (_Float16)fast_exp2(z[i] - mref);
-            lsum += (float)p[i];
+            const float e = fast_exp2(z[i] - mref);
+            const _Float16 hi = (_Float16)e;
+            const _Float16 lo = (_Float16)(e - (float)hi);
+            pw[i] = hi;
+            pw[4 + i] = lo;
+            lsum += (float)hi + (float)lo;   // exact in fp32: the weight the product uses
         }
         // B operand of P.V for dim E n + c: tokens g, g + 4, g + 8, g + 12 (half c of
-        // the rows' chunks)
+        // the rows' chunks), twice -- once against p_hi, once against p_lo
 #pragma unroll
         for (int j = 0; j < G::VW; ++j) {
             const uint32_t w0 = vb[0][j], w1 = vb[1][j], w2 = vb[2][j], w3 = vb[3][j];
-            const uint2 even = {__builtin_amdgcn_perm(w1, w0, 0x05040100u), __builtin_amdgcn_perm(w3, w2, 0x05040100u)};
-            const uint2 odd = {__builtin_amdgcn_perm(w1, w0, 0x07060302u), __builtin_amdgcn_perm(w3, w2, 0x07060302u)};
-            acc[2 * j] = __builtin_amdgcn_mfma_f32_16x16x16f16(p, __builtin_bit_cast(half4_t, even), acc[2 * j], 0, 0, 0);
-            acc[2 * j + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(p, __builtin_bit_cast(half4_t, odd), acc[2 * j + 1], 0, 0, 0);
+            const uint32_t e0 = __builtin_amdgcn_perm(w1, w0, 0x05040100u), e1 = __builtin_amdgcn_perm(w3, w2, 0x05040100u);
+            const uint32_t o0 = __builtin_amdgcn_perm(w1, w0, 0x07060302u), o1 = __builtin_amdgcn_perm(w3, w2, 0x07060302u);
+            const uint4 even = {e0, e1, e0, e1};
+            const uint4 odd = {o0, o1, o0, o1};
+            acc[2 * j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pw, as_half8(even), acc[2 * j], 0, 0, 0);
+            acc[2 * j + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pw, as_half8(odd), acc[2 * j + 1], 0, 0, 0);
         }
     }
 

@@ -75,20 +75,30 @@ class Workload:
                     ctx_sum=int(self.context_lengths.astype(np.int64).sum()))
 
 
-def _fp16_fill(rng: np.random.Generator, shape, dist: str, chunk: int = 1 << 24) -> np.ndarray:
-    """Draw ``prod(shape)`` values in float32 and round to fp16, in sequential chunks
-    (a Generator draws the same stream whether asked for it at once or in pieces)."""
+def _fp16_fill(rng: np.random.Generator, shape, dist: str, chunk: int = 1 << 24,
+               factor: float = 1.0) -> np.ndarray:
+    """Draw ``prod(shape)`` values in float32, multiply them by ``factor`` and round to fp16
+    once, in sequential chunks (a Generator draws the same stream whether asked for it at
+    once or in pieces)."""
     n = int(np.prod(shape))
     out = np.empty(n, dtype=np.float16)
     pos = 0
     while pos < n:
         m = min(chunk, n - pos)
         if dist == "normal":
-            out[pos:pos + m] = rng.standard_normal(m, dtype=np.float32)
+            x = rng.standard_normal(m, dtype=np.float32)
         elif dist == "uniform":
-            out[pos:pos + m] = rng.random(m, dtype=np.float32) * np.float32(2.0) - np.float32(1.0)
+            x = rng.random(m, dtype=np.float32) * np.float32(2.0) - np.float32(1.0)
+        elif dist == "t3":
+            # heavy tails: Student's t with 3 degrees of freedom
+            x = rng.standard_t(3.0, m).astype(np.float32)
         else:
             raise ValueError(f"unknown distribution {dist!r}")
+        if factor != 1.0:
+            x = x * np.float32(factor)
+        if dist == "t3" or factor != 1.0:
+            x = np.clip(x, np.float32(-6e4), np.float32(6e4))   # inside fp16's finite range
+        out[pos:pos + m] = x
         pos += m
     return out.reshape(shape)
 
@@ -99,7 +109,8 @@ def make_workload(*, name: str, batch: int, query_heads: int, kv_heads: int, hea
                   pool: str = "exact", pool_pages: Optional[int] = None, dist: str = "normal",
                   scale: Optional[float] = None, seed: int = 0, canary: bool = True,
                   outlier_fraction: float = 0.0, outlier_factor: float = 8.0,
-                  partition_size: int = 0) -> Workload:
+                  partition_size: int = 0, v_dist: Optional[str] = None, v_factor: float = 1.0,
+                  k_factor: float = 1.0) -> Workload:
     """Build one seeded paged-decode workload.
 
     ``context_lengths`` fixes the lengths; otherwise ``ctx_sampler(rng, batch)`` draws them.
@@ -109,6 +120,10 @@ def make_workload(*, name: str, batch: int, query_heads: int, kv_heads: int, hea
     ``outlier_fraction``: that fraction (rounded) of each sequence's token positions, chosen
     without replacement, has its K rows multiplied by ``outlier_factor`` for every KV head
     (a power of two keeps the product exact in fp16).
+    ``v_dist`` / ``v_factor``: the value rows' distribution ("normal", "uniform" or "t3";
+    default ``dist``) and a factor applied before rounding (wide value rows);
+    ``k_factor``: a factor on the key rows before rounding (a small one gives near-tied
+    scores).  At their defaults the draws are those of ``dist`` alone.
     """
     if query_heads % kv_heads:
         raise ValueError("query_heads must be a multiple of kv_heads")
@@ -147,8 +162,8 @@ def make_workload(*, name: str, batch: int, query_heads: int, kv_heads: int, hea
 
     q = _fp16_fill(rng, (batch, query_heads, head_dim), dist)
     kv_shape = (num_pages, page_size, kv_heads, head_dim)
-    k = _fp16_fill(rng, kv_shape, dist)
-    v = _fp16_fill(rng, kv_shape, dist)
+    k = _fp16_fill(rng, kv_shape, dist, factor=k_factor)
+    v = _fp16_fill(rng, kv_shape, dist if v_dist is None else v_dist, factor=v_factor)
 
     if outlier_fraction > 0.0:
         for b in range(batch):

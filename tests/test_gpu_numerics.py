@@ -1,0 +1,69 @@
+"""GPU parity on value rows far wider than the workloads' N(0, 1), where the error of the
+P.V product's weights shows: |out - ref| grows with the spread of the value rows times
+the weights' relative error.  The kernels carry each weight as two fp16 terms (about 22
+bits), so these inputs must stay well inside the bar |gpu - oracle| <= 1e-3 * (1 + |oracle|):
+the tests ask for at most half of it.  Short contexts (2..16 tokens) with near-tied
+scores are the worst case for a rounded weight (every weight near 1, value rows of both
+signs cancelling); longer ones and heavy-tailed (Student t, 3 degrees of freedom) rows
+are included.  Both routes: the balanced split and fixed partitions (one page, and one
+partition per sequence)."""
+import pytest
+
+from decode_attention_paged_03_amd import pa
+from decode_attention_paged_03_amd import workloads as W
+
+import gpu_common as C
+
+pytestmark = pytest.mark.gpu
+
+MARGIN = 0.5     # worst err/bound allowed here (the bar itself is 1.0)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    pa.load()
+    yield
+
+
+FAMILIES = [
+    # (label, value distribution, value factor, key factor)
+    ("N(0,4)", "normal", 4.0, 1.0),
+    ("N(0,16)", "normal", 16.0, 1.0),
+    ("N(0,16) near-tied", "normal", 16.0, 0.01),
+    ("t3", "t3", 1.0, 1.0),
+    ("4 x t3 near-tied", "t3", 4.0, 0.01),
+]
+SHAPES = [
+    # (query_heads, kv_heads, head_dim, page_size)
+    (32, 8, 128, 16),      # 4 heads per wave (serving shape)
+    (24, 4, 128, 16),      # 6 heads per wave (long-context shape)
+    (8, 2, 64, 8),         # head_dim 64, tiles spanning two pages
+]
+CTX = list(range(2, 17)) + [64, 300, 2000]
+
+
+@pytest.mark.parametrize("family", FAMILIES, ids=lambda f: f[0])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"qh{s[0]}_kvh{s[1]}_d{s[2]}_ps{s[3]}")
+@pytest.mark.parametrize("route", ["balanced", "partition_1page", "single"])
+def test_wide_values(family, shape, route):
+    label, vd, vf, kf = family
+    QH, KVH, D, ps = shape
+    kw = dict(balanced=dict(partition_size=0), partition_1page=dict(partition_size=ps),
+              single=dict(flags=pa.PA_FLAG_FORCE_SINGLE))[route]
+    wl = W.make_workload(name="wide", batch=len(CTX), query_heads=QH, kv_heads=KVH, head_dim=D,
+                         page_size=ps, context_lengths=CTX, pool="holes10",
+                         seed=9300 + 7 * FAMILIES.index(family) + SHAPES.index(shape),
+                         v_dist=vd, v_factor=vf, k_factor=kf)
+    C.say(f"[case] wide values {label} shape {shape} route {route}")
+    dev = C.Device(wl)
+    dec = pa.decoder_for(wl, **kw)
+    try:
+        out = dev.run(dec).cpu().numpy()
+    finally:
+        dec.close()
+    worst = C.check_against_oracle(out, C.oracle.attend_workload(wl, nthreads=C.oracle_threads()),
+                                   f"{label} {shape} {route}")
+    assert worst <= MARGIN, f"{label} {shape} {route}: err/bound {worst:.3f} > {MARGIN}"

@@ -36,18 +36,23 @@ def test_workload_full(name, route):
                        what=f"{name}/{route}")
 
 
-def test_mixed128_sampled():
-    """Mixed large decode at full size, checked on sampled rows: every query head of the
-    longest, the shortest and a spread of sequences (single-tile and split ones)."""
+def test_mixed128_full():
+    """Mixed large decode at full size, every output row (8,192 rows of 128) on both routes:
+    the balanced split and fixed partitions of 1024 tokens (single-tile and split sequences
+    in one launch).  The oracle is evaluated once for both."""
     wl = W.make_named("mixed128")
-    ctx = wl.context_lengths
-    order = np.argsort(ctx, kind="stable")
-    seqs = sorted(set([int(order[0]), int(order[-1]), int(order[len(order) // 2])] +
-                      [int(s) for s in order[::16]]))
-    rows = [b * wl.query_heads + h for b in seqs for h in range(wl.query_heads)]
+    C.say(f"[case] mixed128 full: {wl.summary()}")
+    dev = C.Device(wl)
+    outs = {}
     for part in (0, 1024):
-        C.decode_and_check(wl, rows=rows, partition_size=part,
-                           what=f"mixed128 ({len(seqs)} sequences sampled, partition {part})")
+        dec = pa.decoder_for(wl, partition_size=part)
+        try:
+            outs[part] = dev.run(dec).cpu().numpy()
+        finally:
+            dec.close()
+    ref = C.oracle.attend_workload(wl, nthreads=C.oracle_threads())
+    for part, out in outs.items():
+        C.check_against_oracle(out, ref, f"mixed128 all rows, partition {part}")
 
 
 # ------------------------------------------------------- forced single / split routes
