@@ -45,10 +45,18 @@
  * pa_oracle_append() is the step before attention in a decode loop: it stores the
  * new token's key and value rows in the cache (see its own comment).
  *
+ * pa_oracle_attend_zero_pages() is the same definition with one more reading: a block
+ * table entry outside the pool [0, num_pages) that the context would dereference
+ * reads as a page of zero keys and values (each such token scores 0 and adds a zero
+ * value row).  The first page shows unused table slots as placeholders ("Baseline"
+ * section) and never describes an entry that names no page; this reading is the
+ * engine's debug-bounds mode.  pa_oracle_bad_entries() lists those entries as a
+ * bitmap over the table.
+ *
  * Error handling: return 0 on success; 1 for a bad argument (sizes, null
- * pointers, query_heads % kv_heads != 0); 2 when a context length or a block
- * table entry that would be dereferenced lies outside the pool.  Nothing is
- * read outside the arrays the arguments describe.
+ * pointers, query_heads % kv_heads != 0); 2 when a context length or (outside the
+ * zero-page reading) a block table entry that would be dereferenced lies outside
+ * the pool.  Nothing is read outside the arrays the arguments describe.
  */
 #include <math.h>
 #include <stddef.h>
@@ -81,6 +89,7 @@ typedef struct {
     const uint16_t *q, *k, *v;
     const int32_t *block_tables, *ctx;
     double scale;
+    int zero_pages;   /* entries outside the pool read as zero pages (else an error) */
 } problem_t;
 
 static int check_problem(const problem_t *p)
@@ -95,12 +104,20 @@ static int check_problem(const problem_t *p)
         if (L < 0 || L > (long long)p->max_pages * p->page_size) return 2;
         long long pages = (L + p->page_size - 1) / p->page_size;
         if (pages > 0 && (!p->k || !p->v)) return 1;
-        for (long long lp = 0; lp < pages; ++lp) {
+        for (long long lp = 0; lp < pages && !p->zero_pages; ++lp) {
             int32_t phys = p->block_tables[(size_t)b * p->max_pages + lp];
             if (phys < 0 || phys >= p->num_pages) return 2;
         }
     }
     return 0;
+}
+
+/* Whether token t of sequence b sits in a page of the pool (always, outside the
+ * zero-page reading: check_problem() has rejected every other table). */
+static int in_pool(const problem_t *p, int b, long long t)
+{
+    int32_t phys = p->block_tables[(size_t)b * p->max_pages + t / p->page_size];
+    return phys >= 0 && phys < p->num_pages;
 }
 
 /* Offset of element (token t of sequence b, kv head g, dim 0) in the K / V pool. */
@@ -116,6 +133,7 @@ static size_t kv_offset(const problem_t *p, int b, long long t, int g)
 static double score(const problem_t *p, int b, int h, int g, long long t)
 {
     const uint16_t *qrow = p->q + ((size_t)b * p->query_heads + h) * p->head_dim;
+    if (!in_pool(p, b, t)) return 0.0;                    /* a zero key row scores 0 */
     const uint16_t *krow = p->k + kv_offset(p, b, t, g);
     double dot = 0.0;
     for (int d = 0; d < p->head_dim; ++d)
@@ -141,6 +159,7 @@ static void attend_one(const problem_t *p, int b, int h, double *o, double *s)
     for (long long t = 0; t < L; ++t) {
         double w = exp(s[t] - m);
         z += w;
+        if (!in_pool(p, b, t)) continue;                  /* a zero value row adds nothing */
         const uint16_t *vrow = p->v + kv_offset(p, b, t, g);
         for (int d = 0; d < p->head_dim; ++d) o[d] += w * pa_oracle_half_to_double(vrow[d]);
     }
@@ -183,6 +202,7 @@ static void attend_one_partitioned(const problem_t *p, int b, int h, long long p
         for (long long t = t0; t < t1; ++t) {
             double w = exp(score(p, b, h, g, t) - m_p);
             l_p += w;
+            if (!in_pool(p, b, t)) continue;
             const uint16_t *vrow = p->v + kv_offset(p, b, t, g);
             for (int d = 0; d < p->head_dim; ++d) acc[d] += w * pa_oracle_half_to_double(vrow[d]);
         }
@@ -248,8 +268,51 @@ int pa_oracle_attend(int batch, int query_heads, int kv_heads, int head_dim, int
                      double scale, const int32_t *rows, int n_rows, int nthreads, double *out)
 {
     problem_t p = {batch, query_heads, kv_heads, head_dim, page_size, max_pages, num_pages,
-                   q, k, v, block_tables, ctx, scale};
+                   q, k, v, block_tables, ctx, scale, 0};
     return run(&p, rows, n_rows, 0, nthreads, out);
+}
+
+/* pa_oracle_attend() under the zero-page reading (same arguments). */
+int pa_oracle_attend_zero_pages(int batch, int query_heads, int kv_heads, int head_dim,
+                                int page_size, int max_pages, int num_pages, const uint16_t *q,
+                                const uint16_t *k, const uint16_t *v,
+                                const int32_t *block_tables, const int32_t *ctx, double scale,
+                                const int32_t *rows, int n_rows, int nthreads, double *out)
+{
+    problem_t p = {batch, query_heads, kv_heads, head_dim, page_size, max_pages, num_pages,
+                   q, k, v, block_tables, ctx, scale, 1};
+    return run(&p, rows, n_rows, 0, nthreads, out);
+}
+
+/*
+ * The table entries a decode step dereferences (logical pages lp < ceil(ctx[b] /
+ * page_size) of each sequence) that lie outside the pool [0, num_pages): bit
+ * (b * max_pages + lp) % 32 of word (b * max_pages + lp) / 32 of `bitmap`, which holds
+ * ceil(batch * max_pages / 32) words and is cleared first.  Returns the number of
+ * such entries, or -1 for a bad argument.
+ */
+long long pa_oracle_bad_entries(int batch, int page_size, int max_pages, int num_pages,
+                                const int32_t *block_tables, const int32_t *ctx,
+                                uint32_t *bitmap)
+{
+    if (batch < 0 || page_size <= 0 || max_pages <= 0 || num_pages < 0) return -1;
+    if (batch > 0 && (!block_tables || !ctx || !bitmap)) return -1;
+    long long nbits = (long long)batch * max_pages;
+    memset(bitmap, 0, sizeof(uint32_t) * (size_t)((nbits + 31) / 32));
+    long long count = 0;
+    for (int b = 0; b < batch; ++b) {
+        long long L = ctx[b];
+        if (L < 0 || L > (long long)max_pages * page_size) return -1;
+        long long pages = (L + page_size - 1) / page_size;
+        for (long long lp = 0; lp < pages; ++lp) {
+            int32_t phys = block_tables[(size_t)b * max_pages + lp];
+            if (phys >= 0 && phys < num_pages) continue;
+            long long bit = (long long)b * max_pages + lp;
+            bitmap[bit / 32] |= 1u << (bit % 32);
+            ++count;
+        }
+    }
+    return count;
 }
 
 int pa_oracle_attend_partitioned(int batch, int query_heads, int kv_heads, int head_dim,
@@ -261,7 +324,7 @@ int pa_oracle_attend_partitioned(int batch, int query_heads, int kv_heads, int h
 {
     if (partition_size <= 0) return 1;
     problem_t p = {batch, query_heads, kv_heads, head_dim, page_size, max_pages, num_pages,
-                   q, k, v, block_tables, ctx, scale};
+                   q, k, v, block_tables, ctx, scale, 0};
     return run(&p, rows, n_rows, partition_size, nthreads, out);
 }
 

@@ -37,6 +37,10 @@ def _load(path: Optional[str] = None):
     common = [I, I, I, I, I, I, I, P, P, P, P, P, ctypes.c_double]
     lib.pa_oracle_attend.argtypes = common + [P, I, I, P]
     lib.pa_oracle_attend.restype = I
+    lib.pa_oracle_attend_zero_pages.argtypes = common + [P, I, I, P]
+    lib.pa_oracle_attend_zero_pages.restype = I
+    lib.pa_oracle_bad_entries.argtypes = [I, I, I, I, P, P, P]
+    lib.pa_oracle_bad_entries.restype = ctypes.c_longlong
     lib.pa_oracle_attend_partitioned.argtypes = common + [I, P, I, I, P]
     lib.pa_oracle_attend_partitioned.restype = I
     lib.pa_oracle_append.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P]
@@ -93,12 +97,31 @@ def _call(fn_name, query, key_cache, value_cache, block_tables, context_lengths,
 
 def attend(query, key_cache, value_cache, block_tables, context_lengths, scale: float,
            rows: Optional[Sequence[int]] = None, nthreads: int = 1,
-           lib_path: Optional[str] = None) -> np.ndarray:
+           lib_path: Optional[str] = None, zero_pages: bool = False) -> np.ndarray:
     """Direct definition in fp64.  ``rows``: flat b*query_heads+h indices to evaluate
     (returns [len(rows)][D]); default all (returns [B][QH][D]).  ``lib_path`` selects
-    another build of pa_oracle.c (the tests use it for deliberately broken copies)."""
-    return _call("pa_oracle_attend", query, key_cache, value_cache, block_tables,
-                 context_lengths, scale, rows, nthreads, lib_path=lib_path)
+    another build of pa_oracle.c (the tests use it for deliberately broken copies).
+    ``zero_pages``: table entries outside the pool read as pages of zero keys and values
+    (the debug-bounds reading) instead of being an error."""
+    return _call("pa_oracle_attend_zero_pages" if zero_pages else "pa_oracle_attend", query,
+                 key_cache, value_cache, block_tables, context_lengths, scale, rows, nthreads,
+                 lib_path=lib_path)
+
+
+def bad_entries(block_tables, context_lengths, page_size: int, num_pages: int,
+                lib_path: Optional[str] = None):
+    """(bitmap, count): the dereferenced table entries outside the pool, as uint32 words
+    (bit b * max_pages + lp), and how many there are."""
+    lib = _load(lib_path)
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    ctx = np.ascontiguousarray(context_lengths, dtype=np.int32)
+    B, max_pages = bt.shape
+    bitmap = np.zeros((B * max_pages + 31) // 32, dtype=np.uint32)
+    n = lib.pa_oracle_bad_entries(B, int(page_size), max_pages, int(num_pages), bt.ctypes.data,
+                                  ctx.ctypes.data, bitmap.ctypes.data)
+    if n < 0:
+        raise ValueError("oracle: bad argument")
+    return bitmap, int(n)
 
 
 def attend_partitioned(query, key_cache, value_cache, block_tables, context_lengths,

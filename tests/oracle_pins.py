@@ -52,6 +52,18 @@ class OracleUnderTest:
     def half(self, bits):
         return O.half_to_double(bits, lib_path=self.lib_path)
 
+    def attend_zero_pages(self, wl, **over):
+        a = dict(query=wl.query, key_cache=wl.key_cache, value_cache=wl.value_cache,
+                 block_tables=wl.block_tables, context_lengths=wl.context_lengths,
+                 scale=wl.scale)
+        a.update(over)
+        return O.attend(a["query"], a["key_cache"], a["value_cache"], a["block_tables"],
+                        a["context_lengths"], a["scale"], lib_path=self.lib_path,
+                        zero_pages=True)
+
+    def bad_entries(self, bt, ctx, page_size, num_pages):
+        return O.bad_entries(bt, ctx, page_size, num_pages, lib_path=self.lib_path)
+
     def append(self, new_k, new_v, bt, pos, k, v):
         return O.append(new_k, new_v, bt, pos, k, v, lib_path=self.lib_path)
 
@@ -397,8 +409,63 @@ def pin_append_skips_unaddressable(ot):
     assert np.array_equal(v2.view(np.uint16), v.view(np.uint16))
 
 
+def plant_bad_entries(wl, seed, values):
+    """A copy of wl's block table with entries outside the pool planted at chosen slots:
+    (returns table, dereferenced slots, slots past the context).  Dereferenced slots are
+    logical pages below ceil(ctx / page_size); the values cycle through ``values``."""
+    rng = np.random.default_rng(seed)
+    bt = wl.block_tables.copy()
+    ps, mp = wl.page_size, wl.max_pages_per_sequence
+    inside, past = [], []
+    k = 0
+    for b in range(wl.batch):
+        n = (int(wl.context_lengths[b]) + ps - 1) // ps
+        for lp in sorted(rng.choice(n, size=min(n, 2), replace=False)) if n else []:
+            bt[b, lp] = values[k % len(values)]
+            inside.append((b, int(lp)))
+            k += 1
+        if n < mp:
+            bt[b, n] = values[k % len(values)]            # never dereferenced
+            past.append((b, n))
+            k += 1
+    return bt, inside, past
+
+
+def pin_zero_page_reading(ot):
+    """Under the zero-page reading, a table entry outside the pool gives the same result,
+    bit for bit, as the ordinary definition with that entry pointing at a real page of
+    zeros appended to the pool; with no such entry both readings agree bitwise."""
+    wl = tiny(1500, B=3, QH=4, KVH=2, D=8, ps=4, ctx=[9, 16, 5], max_pages=6, canary=False)
+    assert np.array_equal(ot.attend_zero_pages(wl), ot.attend(wl))
+    npg = wl.num_pages
+    bt, inside, _ = plant_bad_entries(wl, 1501, [-1, npg, npg + 7, 2**31 - 1, -2**31])
+    assert inside
+    zk = np.concatenate([wl.key_cache, np.zeros_like(wl.key_cache[:1])])
+    zv = np.concatenate([wl.value_cache, np.zeros_like(wl.value_cache[:1])])
+    bt_zero = np.where((bt < 0) | (bt >= npg), npg, bt).astype(np.int32)
+    got = ot.attend_zero_pages(wl, block_tables=bt)
+    want = ot.attend(wl, block_tables=bt_zero, key_cache=zk, value_cache=zv)
+    assert np.array_equal(got, want), "zero-page reading differs from a real zero page"
+    assert not np.array_equal(got, ot.attend(wl)), "the planted entries changed nothing"
+
+
+def pin_bad_entry_bitmap(ot):
+    """The bitmap of bad entries holds exactly the planted dereferenced slots: not the
+    planted slots past each context, and nothing for a clean table."""
+    wl = tiny(1600, B=4, QH=4, KVH=2, D=8, ps=4, ctx=[9, 16, 1, 13], max_pages=7)
+    mp, npg = wl.max_pages_per_sequence, wl.num_pages
+    bitmap, n = ot.bad_entries(wl.block_tables, wl.context_lengths, wl.page_size, npg)
+    assert n == 0 and not bitmap.any()
+    bt, inside, past = plant_bad_entries(wl, 1601, [-1, npg, npg + 1, 2**31 - 1])
+    bitmap, n = ot.bad_entries(bt, wl.context_lengths, wl.page_size, npg)
+    bits = {i for i in range(wl.batch * mp) if (int(bitmap[i // 32]) >> (i % 32)) & 1}
+    assert bits == {b * mp + lp for b, lp in inside}, (bits, inside, past)
+    assert n == len(inside)
+
+
 ALL_PINS = [pin_half_exhaustive, pin_dense_library, pin_unpaged_identity,
             pin_page_relabel_bitwise, pin_single_token, pin_equal_keys_mean,
             pin_two_token_logistic, pin_hull_and_linearity, pin_large_shift, pin_outlier_keys,
             pin_partition_identity, pin_canaries_unread, pin_layout_golden, pin_errors_and_empty,
-            pin_append_numpy_scatter, pin_append_rebuilds_cache, pin_append_skips_unaddressable]
+            pin_append_numpy_scatter, pin_append_rebuilds_cache, pin_append_skips_unaddressable,
+            pin_zero_page_reading, pin_bad_entry_bitmap]

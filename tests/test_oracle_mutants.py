@@ -40,6 +40,14 @@ MUTANTS = [
      "size_t src = ((size_t)g * batch + b)"),
     ("append_first_sequence_dropped", "for (int b = 0; b < batch; ++b) {\n        long long pos",
      "for (int b = 1; b < batch; ++b) {\n        long long pos"),
+    ("zero_page_not_counted", "z += w;\n        if (!in_pool(p, b, t)) continue;",
+     "if (!in_pool(p, b, t)) continue;\n        z += w;"),
+    ("zero_page_scores_minus_inf", "if (!in_pool(p, b, t)) return 0.0;",
+     "if (!in_pool(p, b, t)) return -INFINITY;"),
+    ("bad_entries_one_past_context", "for (long long lp = 0; lp < pages; ++lp) {\n            int32_t phys = block_tables",
+     "for (long long lp = 0; lp <= pages && lp < max_pages; ++lp) {\n            int32_t phys = block_tables"),
+    ("bad_entries_negative_kept", "if (phys >= 0 && phys < num_pages) continue;",
+     "if (phys < num_pages) continue;"),
     ("dot_skips_last_dim", "for (int d = 0; d < p->head_dim; ++d)\n        dot +=",
      "for (int d = 0; d + 1 < p->head_dim; ++d)\n        dot +="),
 ]
