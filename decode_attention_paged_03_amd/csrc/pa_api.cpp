@@ -54,7 +54,7 @@ int build_plan(const pa_problem* in, Plan* pl) {
         p.max_context_length < 0)
         return PA_ERR_INVALID_ARGUMENT;
     if (p.query_heads % p.kv_heads) return PA_ERR_INVALID_ARGUMENT;
-    const uint32_t known = PA_FLAG_FORCE_SPLIT | PA_FLAG_FORCE_SINGLE;
+    const uint32_t known = PA_FLAG_FORCE_SPLIT | PA_FLAG_FORCE_SINGLE | PA_FLAG_DEBUG_BOUNDS;
     if (p.flags & ~known) return PA_ERR_INVALID_ARGUMENT;
     if ((p.flags & PA_FLAG_FORCE_SPLIT) && (p.flags & PA_FLAG_FORCE_SINGLE))
         return PA_ERR_INVALID_ARGUMENT;
@@ -78,8 +78,13 @@ int build_plan(const pa_problem* in, Plan* pl) {
     // Its tile indices are 32-bit: all (sequence, KV head, chunk) streams together hold
     // fewer than 2^31 tiles of 16 tokens.
     const long long max_tiles = (long long)p.batch * p.kv_heads * out.n_chunks * ((p.max_context_length + 15LL) / 16);
-    out.balanced = p.partition_size == 0 && p.flags == 0 && p.batch <= kMaxBalancedBatch &&
+    const uint32_t route_flags = p.flags & (PA_FLAG_FORCE_SPLIT | PA_FLAG_FORCE_SINGLE);
+    out.balanced = p.partition_size == 0 && route_flags == 0 && p.batch <= kMaxBalancedBatch &&
                    max_tiles <= INT32_MAX;
+    out.debug_bounds = (p.flags & PA_FLAG_DEBUG_BOUNDS) != 0;
+    // the bitmap has one bit per table entry
+    if (out.debug_bounds && (long long)p.batch * p.max_pages_per_sequence > (1LL << 40))
+        return PA_ERR_UNSUPPORTED;
 
     int partition = p.partition_size;
     if (p.flags & PA_FLAG_FORCE_SINGLE) {
@@ -128,8 +133,15 @@ int build_plan(const pa_problem* in, Plan* pl) {
 }
 
 WsLayout workspace_layout(const Plan& pl, int wg_slots) {
-    WsLayout l{0, 0, 0, wg_slots};
-    if (!pl.need_merge) return l;
+    WsLayout l{0, 0, 0, 0, 0, wg_slots};
+    if (pl.debug_bounds) {
+        l.bitmap_words = ((size_t)pl.prob.batch * (size_t)pl.prob.max_pages_per_sequence + 31) / 32;
+        l.acc_offset = (l.bitmap_words * 4 + 255) / 256 * 256;
+    }
+    if (!pl.need_merge) {
+        l.ml_offset = l.desc_offset = l.bytes = l.acc_offset;
+        return l;
+    }
     size_t rows;
     if (pl.balanced) {
         // Rows of D floats (plus a (max, sum) pair each): per workgroup, two sides x spw
@@ -140,7 +152,7 @@ WsLayout workspace_layout(const Plan& pl, int wg_slots) {
         // one triple per (sequence, query head, partition)
         rows = (size_t)pl.prob.batch * pl.prob.query_heads * (size_t)pl.n_part_max;
     }
-    l.ml_offset = rows * (size_t)pl.prob.head_dim * sizeof(float);
+    l.ml_offset = l.acc_offset + rows * (size_t)pl.prob.head_dim * sizeof(float);
     l.desc_offset = l.ml_offset + rows * 2 * sizeof(float);
     l.bytes = l.desc_offset + (pl.balanced ? (size_t)wg_slots * 2 * 16 : 0);
     l.wg_slots = wg_slots;
@@ -218,8 +230,9 @@ pa_status pa_decode_noalloc(const pa_handle* handle, const void* query, const vo
                                            context_lengths, scale, out);
     if (st != PA_OK) return st;
     const pa::Plan& pl = handle->plan;
+    if (pl.debug_bounds) return PA_ERR_INVALID_ARGUMENT;   // its bitmap needs a caller workspace
     void* scratch = nullptr;
-    pa::WsLayout layout{0, 0, 0, 0};
+    pa::WsLayout layout{0, 0, 0, 0, 0, 0};
     if (pl.need_merge) {
         // the balanced route's rows are indexed by workgroup: sized for this device's grid
         const int slots = pl.balanced ? pa::device_compute_units() : 0;

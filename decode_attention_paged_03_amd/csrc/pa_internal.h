@@ -47,6 +47,7 @@ struct Plan {
     // both
     int ps_log2;            // log2(page_size)
     bool need_merge;        // a merge kernel is launched
+    bool debug_bounds;      // PA_FLAG_DEBUG_BOUNDS: record table entries outside the pool
     size_t rows_per_wg;     // balanced route: partial rows per workgroup (2 sides x spw x heads)
     size_t ws_bytes;        // workspace bytes pa_workspace_size() reports (0 when need_merge is
                             // false): the layout for kMaxBalancedWG workgroups
@@ -59,9 +60,12 @@ struct Plan {
 // caller-provided workspace is sized for kMaxBalancedWG (no device query on the host), the
 // library's own scratch (pa_decode_noalloc) for the device's compute units.
 struct WsLayout {
+    size_t bitmap_words;    // PA_FLAG_DEBUG_BOUNDS: uint32 words of the bad-entry bitmap at
+                            // offset 0 (0 without the flag)
+    size_t acc_offset;      // byte offset of the partial rows (the bitmap rounded to 256 B)
     size_t ml_offset;       // byte offset of the (max, sum) pairs
     size_t desc_offset;     // balanced route: byte offset of the per-workgroup merge records
-    size_t bytes;           // total (0 when no merge is launched)
+    size_t bytes;           // total (0 when no merge is launched and no bitmap is kept)
     int wg_slots;           // balanced route: workgroups the partial rows are sized for
 };
 WsLayout workspace_layout(const Plan& plan, int wg_slots);

@@ -118,7 +118,14 @@ struct DecodeArgs {
     int batch, query_heads, kv_heads, group, n_chunks, max_pages, partition, n_part_max, ps_log2;
     int force_split;
     int spw, waves_per_stream, bands;   // balanced route (see Plan)
+    int num_pages;          // pages in the pool: table entries outside [0, num_pages) read as zeros
 };
+
+// A table entry outside the pool [0, num_pages) names no page: it becomes -1, which the
+// tile loads treat as a page of zeros (a zero buffer range, so nothing is read).
+__device__ __forceinline__ int pool_page(int entry, int num_pages) {
+    return (uint32_t)entry < (uint32_t)num_pages ? entry : -1;
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -206,7 +213,8 @@ __device__ __forceinline__ void buf_ldv(__amdgpu_buffer_rsrc_t r, uint32_t off, 
 // Loads of one 16-token tile.  `kp`/`vp` point at the K/V row (this KV head) of the
 // tile's first token; with pages of 8 the tile's tokens 8..15 sit in the next page, whose
 // rows start at `kp2`/`vp2`.  Tokens past n_valid (0..16, wave-uniform) read as zero:
-// their scores are masked, and their zero V rows add nothing.
+// their scores are masked, and their zero V rows add nothing.  ok1 / ok2 (wave-uniform):
+// whether the first / second page is in the pool; a page that is not reads as zeros.
 //   K: kb[j] = 16 bytes of row ktok, dims 32 j + 8 g .. + 7 (koff = ktok * tok + 16 g);
 //      with KROW (D = 128) K is loaded like V instead: kb[i] = dims 8 n .. 8 n + 7 of row
 //      4 i + g (koff = voff), whole rows per instruction, and regrouped through LDS.
@@ -214,12 +222,12 @@ __device__ __forceinline__ void buf_ldv(__amdgpu_buffer_rsrc_t r, uint32_t off, 
 template <int D, bool SPLIT, bool KROW = false>
 __device__ __forceinline__ void load_kv(const char* kp, const char* vp, const char* kp2, const char* vp2,
                                         uint32_t koff, uint32_t voff, uint32_t tok_bytes, int n_valid,
-                                        const Lane& L, uint4 (&kb)[Geo<D>::UK],
+                                        bool ok1, bool ok2, const Lane& L, uint4 (&kb)[Geo<D>::UK],
                                         uint32_t (&vb)[4][Geo<D>::VW]) {
     using G = Geo<D>;
     n_valid = __builtin_amdgcn_readfirstlane(n_valid);   // uniform; keeps the resource in SGPRs
     if constexpr (!SPLIT) {
-        const int bytes = n_valid * (int)tok_bytes;
+        const int bytes = ok1 ? n_valid * (int)tok_bytes : 0;
         const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kp, bytes);
         const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vp, bytes);
         if constexpr (KROW) {
@@ -232,7 +240,7 @@ __device__ __forceinline__ void load_kv(const char* kp, const char* vp, const ch
 #pragma unroll
         for (int i = 0; i < 4; ++i) buf_ldv<G::VW>(rv, voff, 4 * i * tok_bytes, vb[i]);
     } else {
-        const int n1 = min(n_valid, 8), n2 = max(n_valid - 8, 0);
+        const int n1 = ok1 ? min(n_valid, 8) : 0, n2 = ok2 ? max(n_valid - 8, 0) : 0;
         const __amdgpu_buffer_rsrc_t rk1 = tile_rsrc(kp, n1 * (int)tok_bytes);
         const __amdgpu_buffer_rsrc_t rk2 = tile_rsrc(kp2, n2 * (int)tok_bytes);
         const __amdgpu_buffer_rsrc_t rv1 = tile_rsrc(vp, n1 * (int)tok_bytes);
@@ -465,7 +473,7 @@ pa_decode_kernel(DecodeArgs a) {
     const int pg0 = t_begin >> ps_log2;
     const int npg = ((t_end - 1) >> ps_log2) - pg0 + 1;
     const int32_t* bt_row = a.bt + (size_t)b * a.max_pages + pg0;
-    for (int i = tid; i < npg; i += NW * 64) s_bt[i] = bt_row[i];
+    for (int i = tid; i < npg; i += NW * 64) s_bt[i] = pool_page(bt_row[i], a.num_pages);
 
     uint4 qb[G::UK];
     load_q_raw<D, HP>(a.q, row0, L, qb);
@@ -491,16 +499,21 @@ pa_decode_kernel(DecodeArgs a) {
     auto load_tile = [&](int k, uint4 (&kb)[G::UK], uint32_t (&vb)[4][G::VW]) {
         const int t0 = t_begin + (wave + k * NW) * T;
         const int pg = (t0 >> ps_log2) - pg0;
-        const int phys = __builtin_amdgcn_readfirstlane(s_bt[pg]);
-        const size_t base = (size_t)phys * page_bytes + (size_t)(t0 & ((1 << ps_log2) - 1)) * tok_bytes;
+        const int phys = __builtin_amdgcn_readfirstlane(s_bt[pg]);   // -1: outside the pool
+        const size_t base = (size_t)max(phys, 0) * page_bytes + (size_t)(t0 & ((1 << ps_log2) - 1)) * tok_bytes;
         size_t base2 = base;
+        int phys2 = phys;
         if constexpr (SPLIT) {
             // tokens 8..15 of the tile sit in the next page, which exists only when the
             // tile reaches past token 8
-            if (t0 + 8 < t_end) base2 = (size_t)__builtin_amdgcn_readfirstlane(s_bt[pg + 1]) * page_bytes;
+            if (t0 + 8 < t_end) {
+                phys2 = __builtin_amdgcn_readfirstlane(s_bt[pg + 1]);
+                base2 = (size_t)max(phys2, 0) * page_bytes;
+            }
         }
         load_kv<D, SPLIT>(kbase + base, vbase + base, kbase + base2, vbase + base2, koff, voff,
-                          (uint32_t)tok_bytes, max(0, min(T, t_end - t0)), L, kb, vb);
+                          (uint32_t)tok_bytes, max(0, min(T, t_end - t0)), phys >= 0, phys2 >= 0, L,
+                          kb, vb);
     };
 
     if (nk > 0) {
@@ -950,6 +963,8 @@ pa_decode_balanced(DecodeArgs a) {
         // tile and drains all loads before each tile's page lookup.  This path runs once
         // per 64 tiles.
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        btv = pool_page(btv, a.num_pages);
+        if constexpr (SPLIT) btv2 = pool_page(btv2, a.num_pages);
     };
 
     // A wave-uniform cursor over the units to load, and the description of a loaded tile.
@@ -1008,14 +1023,18 @@ pa_decode_balanced(DecodeArgs a) {
         d.T = cT;
         d.n_valid = min(T, cctx - tok);
         d.first = (i == 0) || (cl == 0);
-        const int phys = __builtin_amdgcn_readlane(btv, i & 63);
-        const size_t base = (size_t)phys * page_bytes + (size_t)(tok & ((1 << ps_log2) - 1)) * tok_bytes;
+        const int phys = __builtin_amdgcn_readlane(btv, i & 63);   // -1: outside the pool
+        const size_t base = (size_t)max(phys, 0) * page_bytes + (size_t)(tok & ((1 << ps_log2) - 1)) * tok_bytes;
         size_t base2 = base;
-        if constexpr (SPLIT) base2 = (size_t)__builtin_amdgcn_readlane(btv2, i & 63) * page_bytes;
+        int phys2 = phys;
+        if constexpr (SPLIT) {
+            phys2 = __builtin_amdgcn_readlane(btv2, i & 63);
+            base2 = (size_t)max(phys2, 0) * page_bytes;
+        }
         const char* kbase = a.k + (size_t)ckvh * D * 2;
         const char* vbase = a.v + (size_t)ckvh * D * 2;
         load_kv<D, SPLIT, KROW>(kbase + base, vbase + base, kbase + base2, vbase + base2, koff, voff,
-                                (uint32_t)tok_bytes, d.n_valid, L, kb, vb);
+                                (uint32_t)tok_bytes, d.n_valid, phys >= 0, phys2 >= 0, L, kb, vb);
         if (d.first) load_q_raw<D, HP>(a.q, (size_t)cb * a.query_heads + ckvh * a.group + cchunk * HP, L, qr);
     };
 
@@ -1540,6 +1559,27 @@ pa_merge_balanced(DecodeArgs a) {
     }
 }
 
+// PA_FLAG_DEBUG_BOUNDS: word w of the bitmap holds the bits of table entries 32 w ..
+// 32 w + 31 (row-major, b * max_pages + logical page) that a context dereferences (logical
+// page < ceil(ctx[b] / page_size)) and that lie outside the pool.  One thread writes each
+// word whole, so the bitmap needs no clearing pass and no atomics.
+__global__ void __launch_bounds__(256)
+pa_bad_entries_kernel(const int32_t* bt, const int32_t* ctx, int max_pages, int ps_log2, int num_pages,
+                      uint32_t* bits, long long words, long long entries) {
+    const long long w = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (w >= words) return;
+    uint32_t word = 0;
+    for (int i = 0; i < 32; ++i) {
+        const long long e = 32 * w + i;
+        if (e >= entries) break;
+        const long long b = e / max_pages;
+        const long long lp = e - b * max_pages;
+        const long long pages = ((long long)ctx[b] + (1 << ps_log2) - 1) >> ps_log2;
+        if (lp < pages && (uint32_t)bt[e] >= (uint32_t)num_pages) word |= 1u << i;
+    }
+    bits[w] = word;
+}
+
 #ifndef PA_WAVES
 #define PA_WAVES 4   // waves per decode workgroup (fixed route)
 #endif
@@ -1662,9 +1702,18 @@ hipError_t launch(const Plan& pl, const void* q, const void* k, const void* v,
     float* ws_ml = nullptr;
     int4* ws_desc = nullptr;
     if (pl.need_merge) {
-        ws_acc = static_cast<float*>(workspace);
+        ws_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + layout.acc_offset);
         ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + layout.ml_offset);
         if (pl.balanced) ws_desc = reinterpret_cast<int4*>(static_cast<char*>(workspace) + layout.desc_offset);
+    }
+    if (pl.debug_bounds) {
+        const long long words = (long long)layout.bitmap_words;
+        hipLaunchKernelGGL(pa_bad_entries_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, stream,
+                           block_tables, ctx, p.max_pages_per_sequence, pl.ps_log2, p.num_physical_pages,
+                           static_cast<uint32_t*>(workspace), words,
+                           (long long)p.batch * p.max_pages_per_sequence);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
     DecodeArgs da;
     da.q = static_cast<const _Float16*>(q);
@@ -1691,6 +1740,7 @@ hipError_t launch(const Plan& pl, const void* q, const void* k, const void* v,
     da.spw = pl.spw;
     da.waves_per_stream = pl.waves_per_stream;
     da.bands = pl.bands;
+    da.num_pages = p.num_physical_pages;
 
     hipError_t err = (p.head_dim == 128) ? launch_decode_d<128>(pl, da, layout.wg_slots, stream)
                                          : launch_decode_d<64>(pl, da, layout.wg_slots, stream);

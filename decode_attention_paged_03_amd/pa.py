@@ -29,6 +29,7 @@ PA_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 PA_FLAG_FORCE_SPLIT = 0x1
 PA_FLAG_FORCE_SINGLE = 0x2
+PA_FLAG_DEBUG_BOUNDS = 0x4
 
 EXPORTED = ("pa_create", "pa_workspace_size", "pa_decode", "pa_decode_noalloc", "pa_append",
             "pa_destroy", "pa_status_string")
@@ -179,6 +180,19 @@ class PagedDecoder:
                   block_tables.data_ptr(), context_lengths.data_ptr(), scale, out.data_ptr(),
                   ws.data_ptr() if ws is not None else 0, self.workspace_bytes, stream.cuda_stream)
         return out
+
+    def bad_entry_bitmap(self):
+        """With PA_FLAG_DEBUG_BOUNDS: the bitmap the last call left at the start of the
+        workspace, as numpy uint32 words (bit i of word w: table entry 32 w + i, row-major),
+        copied to the host after the device has finished."""
+        import numpy as np
+        import torch
+        p = self.problem
+        if not (p.flags & PA_FLAG_DEBUG_BOUNDS):
+            raise ValueError("the problem was created without PA_FLAG_DEBUG_BOUNDS")
+        words = (p.batch * p.max_pages_per_sequence + 31) // 32
+        torch.cuda.synchronize(self.workspace.device)
+        return self.workspace[:4 * words].cpu().numpy().view(np.uint32).copy()
 
     def append(self, new_key, new_value, key_cache, value_cache, block_tables, positions,
                stream=None):

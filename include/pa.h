@@ -71,6 +71,18 @@ typedef enum pa_status {
 /* Flags for pa_problem.flags */
 #define PA_FLAG_FORCE_SPLIT  0x1u /* route every sequence through partition triples + merge */
 #define PA_FLAG_FORCE_SINGLE 0x2u /* one partition per sequence (partition = max context)     */
+/* Record block-table entries outside the pool.  Every call treats a table entry that a
+ * context dereferences but that lies outside [0, num_physical_pages) as a page of zero
+ * keys and values: it is never read, so it cannot fault.  (The first page's "Baseline"
+ * section shows unused table slots as placeholders and never describes an entry that
+ * names no page.)  With this flag, pa_decode() also records each such entry: the
+ * workspace then begins with a bitmap of batch * max_pages_per_sequence bits in
+ * little-endian uint32 words, with bit i of word w for table entry 32 w + i (row-major,
+ * entry b * max_pages_per_sequence + logical page).  The call clears the bitmap, then
+ * sets the bit of every dereferenced entry outside the pool.  The caller reads the
+ * words after the stream passes the call.  pa_workspace_size() includes them, rounded up
+ * to 256 bytes. */
+#define PA_FLAG_DEBUG_BOUNDS 0x4u
 
 typedef struct pa_problem {
     int32_t batch;                  /* number of sequences, >= 1                                  */
@@ -91,11 +103,18 @@ typedef struct pa_problem {
 typedef struct pa_handle pa_handle; /* opaque, host memory only */
 
 /* Validate *problem and create a handle holding a copy of it plus the launch plan.
- * Host only: no HIP call.  On error *out is set to NULL. */
+ * The problem struct is the shape description of the launchers in the first page's
+ * "Baseline" to "V4" sections (batch, query and KV heads, head_dim, page_size, table row
+ * stride), plus the pool size, the split and the flags.  Host only: no HIP call.  On
+ * error *out is set to NULL. */
 pa_status pa_create(const pa_problem *problem, pa_handle **out);
 
-/* Bytes of device workspace pa_decode() needs for this problem (0 when no sequence can
- * need more than one partition).  Host only. */
+/* Bytes of device workspace pa_decode() needs for this problem.  The workspace holds the
+ * partial (max, sum, output) triples of a split context, as in the split kernel of the
+ * first page's "V4 (Context-axis parallelism)" section, whose launcher leaves workspace
+ * ownership to its caller; with PA_FLAG_DEBUG_BOUNDS the bad-entry bitmap comes first.
+ * 0 when no sequence can need more than one partition and the flag is not set.  Host
+ * only. */
 pa_status pa_workspace_size(const pa_handle *handle, size_t *bytes);
 
 /* Enqueue one decode step on `stream`.
@@ -109,10 +128,13 @@ pa_status pa_workspace_size(const pa_handle *handle, size_t *bytes);
  *                   written (a sequence with context length 0 gets zeros)
  *   workspace       device scratch of at least pa_workspace_size() bytes, 16-byte aligned
  *                   (may be NULL when that size is 0); contents undefined afterwards
- * Preconditions (not checked): 0 <= context_lengths[b] <= max_context_length, and
- * 0 <= block_tables[b][i] < number of pages for i < ceil(context_lengths[b] / page_size).
- * Table slots past that are never read.  Pointers are device pointers (or host-mapped
- * memory the GPU can read). */
+ * Precondition (not checked): 0 <= context_lengths[b] <= max_context_length.  Table
+ * entries i < ceil(context_lengths[b] / page_size) should lie in [0, num_physical_pages):
+ * one that does not reads as a page of zeros (see PA_FLAG_DEBUG_BOUNDS).  Table slots past
+ * that are never read.  Pointers are device pointers (or host-mapped memory the GPU can
+ * read).  The step is the "Paged Attention" definition above, evaluated as the first
+ * page's Baseline recurrence with the "V4" split and merge (and the commit page's
+ * single-tile path for contexts that need no merge). */
 pa_status pa_decode(const pa_handle *handle, const void *query, const void *key_cache,
                     const void *value_cache, const int32_t *block_tables,
                     const int32_t *context_lengths, float scale, float *out, void *workspace,
@@ -127,7 +149,9 @@ pa_status pa_decode(const pa_handle *handle, const void *query, const void *key_
  * hipFree or allocating library routine), copies to or from the host or synchronises.
  * Returns PA_ERR_SCRATCH, before enqueuing anything, when the problem needs more workspace
  * than the array holds (e.g. fixed partitions over a large batch; the default route of
- * every supported shape fits on a GPU of up to 320 compute units).
+ * every supported shape fits on a GPU of up to 320 compute units), and
+ * PA_ERR_INVALID_ARGUMENT for a problem with PA_FLAG_DEBUG_BOUNDS (its bitmap needs a
+ * workspace the caller can read).
  * All calls on one GPU share its array, and the array keeps the last call's contents: two
  * calls that may run at the same time on one GPU (two streams, two threads without
  * ordering) race and corrupt each other's results.  Order them on one stream. */
@@ -158,10 +182,12 @@ pa_status pa_append(const pa_handle *handle, const void *new_key, const void *ne
                     void *key_cache, void *value_cache, const int32_t *block_tables,
                     const int32_t *positions, hipStream_t stream);
 
-/* Free the handle; NULL is accepted. */
+/* Free the handle (host memory only; the library holds nothing else per handle, as the
+ * first page's launchers hold nothing between calls).  NULL is accepted. */
 pa_status pa_destroy(pa_handle *handle);
 
-/* Static, NUL-terminated name of a status code. */
+/* Static, NUL-terminated name of a status code (a host-side convenience with no
+ * counterpart on the pages). */
 const char *pa_status_string(int status);
 
 #ifdef __cplusplus

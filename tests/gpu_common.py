@@ -26,9 +26,11 @@ def say(*a):
 class Device:
     """A workload's arrays on the GPU.  With ``guard`` a NaN page sits in front of each
     cache and the pointers handed to the library start one page in, so a stray -1 table
-    entry would read NaN (and fail the comparison) instead of leaving the allocation."""
+    entry would read NaN (and fail the comparison) instead of leaving the allocation.
+    ``guard_after`` more NaN pages follow the pool (table entries just past the pool then
+    also land on allocated NaN)."""
 
-    def __init__(self, wl, guard: bool = True):
+    def __init__(self, wl, guard: bool = True, guard_after: int = 0):
         import torch
         self.wl = wl
         dev = "cuda"
@@ -36,16 +38,19 @@ class Device:
         extra = 1 if guard else 0
 
         def cache(arr):
-            t = torch.empty((wl.num_pages + extra,) + arr.shape[1:], dtype=torch.float16, device=dev)
+            t = torch.empty((wl.num_pages + extra + guard_after,) + arr.shape[1:],
+                            dtype=torch.float16, device=dev)
             if guard:
                 t[0].fill_(float("nan"))
-            t[extra:].copy_(torch.from_numpy(arr))
+            if guard_after:
+                t[extra + wl.num_pages:].fill_(float("nan"))
+            t[extra:extra + wl.num_pages].copy_(torch.from_numpy(arr))
             return t
 
         self.k_alloc = cache(wl.key_cache)
         self.v_alloc = cache(wl.value_cache)
-        self.k = self.k_alloc[extra:]
-        self.v = self.v_alloc[extra:]
+        self.k = self.k_alloc[extra:extra + wl.num_pages]
+        self.v = self.v_alloc[extra:extra + wl.num_pages]
         assert self.k.is_contiguous() and self.k.data_ptr() % 16 == 0 and page * 2 % 16 == 0
         self.q = torch.from_numpy(wl.query).to(dev)
         self.bt = torch.from_numpy(wl.block_tables).to(dev)

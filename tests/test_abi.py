@@ -76,6 +76,9 @@ def create_status(prob):
     (dict(partition_size=16 * 513), pa.PA_ERR_UNSUPPORTED),
     (dict(max_context_length=8 * 16 + 1), pa.PA_ERR_INVALID_ARGUMENT),
     (dict(flags=0x100), pa.PA_ERR_INVALID_ARGUMENT),
+    (dict(flags=0x8), pa.PA_ERR_INVALID_ARGUMENT),
+    (dict(flags=pa.PA_FLAG_DEBUG_BOUNDS), pa.PA_OK),
+    (dict(flags=pa.PA_FLAG_DEBUG_BOUNDS | pa.PA_FLAG_FORCE_SPLIT), pa.PA_OK),
     (dict(flags=pa.PA_FLAG_FORCE_SPLIT | pa.PA_FLAG_FORCE_SINGLE), pa.PA_ERR_INVALID_ARGUMENT),
     (dict(flags=pa.PA_FLAG_FORCE_SINGLE, max_pages_per_sequence=4096), pa.PA_ERR_UNSUPPORTED),
 ])
@@ -121,6 +124,18 @@ def test_workspace_size():
     assert ws_size(partition_size=1024) == 0
     assert ws_size(flags=pa.PA_FLAG_FORCE_SPLIT) == 2 * 8 * 1 * (128 + 2) * 4
     assert ws_size(flags=pa.PA_FLAG_FORCE_SINGLE, max_pages_per_sequence=64) == 0
+
+
+def test_workspace_size_with_bounds_bitmap():
+    # PA_FLAG_DEBUG_BOUNDS puts a bitmap of batch * max_pages bits first, rounded up to 256
+    # bytes; it keeps the balanced route and needs a workspace even without a merge
+    D = pa.PA_FLAG_DEBUG_BOUNDS
+    assert ws_size(flags=D) == 256 + ws_size()
+    assert ws_size(flags=D, partition_size=1024) == 256
+    assert ws_size(flags=D, batch=100, max_pages_per_sequence=100,
+                   num_physical_pages=20000) == 1280 + ws_size(batch=100, max_pages_per_sequence=100,
+                                                               num_physical_pages=20000)
+    assert ws_size(flags=D | pa.PA_FLAG_FORCE_SPLIT) == 256 + ws_size(flags=pa.PA_FLAG_FORCE_SPLIT)
 
 
 def test_decode_rejects_before_any_hip_call(lib):
@@ -177,6 +192,11 @@ def test_decode_noalloc_rejects_before_any_hip_call(lib):
         assert status(scale=float("nan")) == pa.PA_ERR_INVALID_ARGUMENT
         assert status(scale=float("-inf")) == pa.PA_ERR_INVALID_ARGUMENT
         assert lib.pa_decode_noalloc(None, A, A, A, A, A, 0.1, A, None) == pa.PA_ERR_INVALID_ARGUMENT
+        dbg = pa.pa_create(good(flags=pa.PA_FLAG_DEBUG_BOUNDS))
+        try:   # the bad-entry bitmap needs a workspace the caller can read
+            assert lib.pa_decode_noalloc(dbg, A, A, A, A, A, 0.1, A, None) == pa.PA_ERR_INVALID_ARGUMENT
+        finally:
+            pa.pa_destroy(dbg)
     finally:
         pa.pa_destroy(big)
         pa.pa_destroy(small)
