@@ -52,9 +52,16 @@ def parse():
                     help="total K/V bytes to rotate over (cold-cache timing); 0 = one copy")
     ap.add_argument("--append-steps", type=int, default=200,
                     help="calls of pa_append timed after the decode steps (0: skip)")
+    ap.add_argument("--also", default="long100k,small_batch,mixed128,tiny",
+                    help="comma-separated workloads measured after the headline one, each "
+                         "reported in the line's \"workloads\" object ('none': only the headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0,
-                    help="target CPU time of the oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=3.0,
+                    help="target wall time of one oracle evaluation of the headline workload "
+                         "(the other workloads use a third of it)")
+    ap.add_argument("--write-resources", action="store_true",
+                    help="compile the kernels with resource-usage remarks and write "
+                         "profiles/resources.txt (no GPU needed)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for counter calibration)")
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
@@ -302,45 +309,68 @@ def traffic_per_call(workload: str):
         return None
 
 
-def cpu_baseline(wl, target_s: float):
+# The GPU machine gives one GPU a share of 16 host cores; the oracle never uses more threads.
+CPU_SHARE = 16
+
+
+def host_cores() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(wl, target_s: float, modes=("single", "all"), reps: int = 3):
     """Time the fp64 oracle (as it is) on the host cores over a bounded sample of the
-    workload: whole sequences (all query heads) from the front of the batch."""
+    workload: output rows (sequence, query head) taken from the front of the batch until
+    one evaluation should take about ``target_s``.  Each mode (one thread; all threads of
+    the box's share) runs ``reps`` evaluations and reports the median.  A row's KV bytes
+    count 1/group of its KV head's ctx * head_dim * 4 bytes, so whole sequences count what
+    the GPU's KV-bytes metric counts."""
     import numpy as np
     import oracle
-    try:
-        cores = len(os.sched_getaffinity(0))
-    except AttributeError:
-        cores = os.cpu_count() or 1
-    cores = max(1, min(cores, 16))
-    QH = wl.query_heads
-    # probe on the first sequence to size the sample
+    threads_all = max(1, min(host_cores(), CPU_SHARE))
+    ctx = wl.context_lengths.astype(np.int64)
+    QH, G = wl.query_heads, wl.group
+    # rows in b-major order, skipping empty sequences; probe one row of the first non-empty
+    rows_all = [b * QH + h for b in range(wl.batch) if ctx[b] > 0 for h in range(QH)]
+    if not rows_all:
+        return None
     t0 = time.perf_counter()
-    oracle.attend_workload(wl, rows=list(range(QH)), nthreads=cores)
-    probe = time.perf_counter() - t0
-    per_token = probe / max(1, int(wl.context_lengths[0]))
-    budget_tokens = target_s / max(per_token, 1e-12)
-    n, acc = 0, 0
-    while n < wl.batch and acc + int(wl.context_lengths[n]) <= budget_tokens:
-        acc += int(wl.context_lengths[n])
-        n += 1
-    n = max(n, 1)
-    rows = list(range(n * QH))
-    # a sample smaller than the budget (the whole workload fits) is evaluated repeatedly
-    sample_tokens = int(np.asarray(wl.context_lengths[:n], dtype=np.int64).sum())
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.attend_workload(wl, rows=rows, nthreads=cores)
-        reps += 1
-        dt = time.perf_counter() - t0
-        if dt >= 0.75 * target_s or dt * (reps + 1) / reps > 2.0 * target_s:
-            break
-    kv_bytes = sample_tokens * wl.kv_heads * wl.head_dim * 4
-    return {"value": round(kv_bytes * reps / dt / 1e9, 6), "unit": "GB/s", "cores": cores,
+    oracle.attend_workload(wl, rows=rows_all[:1], nthreads=1)
+    per_token_row = (time.perf_counter() - t0) / max(1, int(ctx[rows_all[0] // QH]))
+    out = {}
+    for mode in modes:
+        threads = 1 if mode == "single" else threads_all
+        budget = target_s * threads / max(per_token_row, 1e-12)     # token-rows per evaluation
+        rows, acc = [], 0
+        for r in rows_all:
+            c = int(ctx[r // QH])
+            if rows and acc + c > budget:
+                break
+            rows.append(r)
+            acc += c
+        kv_bytes = acc * wl.head_dim * 4 / G
+        times = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            oracle.attend_workload(wl, rows=rows, nthreads=threads)
+            times.append(time.perf_counter() - t0)
+        dt = float(np.median(times))
+        nseq = len({r // QH for r in rows})
+        out[mode] = {"value": round(kv_bytes / dt / 1e9, 6), "unit": "GB/s", "threads": threads,
+                     "seconds_median": round(dt, 4), "evaluations": reps,
+                     "sample": f"{len(rows)} of {len(rows_all)} output rows (first {nseq} "
+                               f"sequences), {kv_bytes / 1e6:.2f} MB of K/V"}
+    main_mode = "all" if "all" in out else "single"
+    m = out[main_mode]
+    line = {"value": m["value"], "unit": "GB/s", "cores": m["threads"], "host_cores": host_cores(),
             "kind": "oracle",
-            "sample": f"first {n} of {wl.batch} sequences (all {QH} query heads, "
-                      f"{kv_bytes / 1e6:.1f} MB of K/V) x {reps} evaluation(s), {dt:.1f} s wall, "
-                      f"{cores} OpenMP threads"}
+            "sample": f"{m['sample']}, median of {m['evaluations']} evaluation(s) on "
+                      f"{m['threads']} OpenMP thread(s) (threads capped at the GPU box's "
+                      f"{CPU_SHARE}-core share)"}
+    line.update({k: v for k, v in out.items()})
+    return line
 
 
 def measure_append(dec, wl, k, v, bt, stream, steps: int):
@@ -402,36 +432,75 @@ def measure_append(dec, wl, k, v, bt, stream, steps: int):
                       f"(eager: {steps} back-to-back calls)"}
 
 
-def main():
-    args = parse()
-    if args.summarize_trace:
-        print(summarize_trace(args.summarize_trace, args.workload))
-        return
-    if args.summarize_pmc:
-        print(summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload))
-        return
-    if args.summarize_counters:
-        print(summarize_counters(args.summarize_counters, args.workload))
-        return
-    if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
-              "run with --gpus 1", file=sys.stderr)
-        sys.exit(2)
+def resources_path() -> str:
+    return os.path.join(PROFILES, "resources.txt")
+
+
+def write_resources() -> str:
+    """Compile the kernels with clang's resource-usage remarks (registers, scratch,
+    occupancy, LDS per kernel) into profiles/resources.txt, keyed by the kernel sources'
+    hash.  Needs no GPU."""
+    import tempfile
+    from decode_attention_paged_03_amd import build as B
+    with tempfile.TemporaryDirectory() as d:
+        B.build(asm_dir=d, out=os.path.join(d, "libpa.so"), build_dir=os.path.join(d, "_build"))
+        with open(os.path.join(d, "resource_usage.txt")) as f:
+            table = B.resource_table(f.read())
+    lines = ["# Resource usage of the kernels (clang -Rpass-analysis=kernel-resource-usage, gfx950)",
+             f"kernel_source_sha256: {kernel_source_hash()}",
+             "command: python bench.py --write-resources",
+             "(template arguments: decode kernels <head_dim, heads per wave, tile buffers, waves, "
+             "pages of 8, whole-row K>; sgpr/vgpr/agpr per wave, scratch bytes per lane, "
+             "waves/simd the registers allow, lds bytes per workgroup)",
+             table]
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(resources_path(), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return resources_path()
+
+
+def kernel_resources(kernel_names):
+    """Rows of profiles/resources.txt for the given kernels (e.g. 'pa_decode_balanced<128,4,1,12,0,1>'),
+    or None when the file is absent or was written for other kernel sources."""
+    path = resources_path()
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        text = f.read()
+    m = re.search(r"kernel_source_sha256: (\w+)", text)
+    if not m or m.group(1) != kernel_source_hash():
+        return None
+    lines = text.splitlines()
+    hdr = next((l for l in lines if l.startswith("kernel ")), None)
+    if hdr is None:
+        return None
+    cols = hdr.split()[1:]
+    out = {}
+    for l in lines:
+        parts = l.split()
+        if parts and parts[0] in kernel_names:
+            out[parts[0]] = dict(zip(cols, (int(x) for x in parts[1:])))
+    return out or None
+
+
+def decode_kernel_names(dec, wl):
+    """Names (as in profiles/resources.txt) of the kernels one pa_decode call runs on the
+    default (balanced) route: heads per wave = the largest divisor of the group up to 8;
+    pages of 8 split a tile; whole-row K loads at head_dim 128 (when the LDS fits)."""
+    hp = max(h for h in range(1, 9) if wl.group % h == 0)
+    split = 1 if wl.page_size < 16 else 0
+    krow = 1 if wl.head_dim == 128 else 0
+    return [f"pa_decode_balanced<{wl.head_dim},{hp},1,12,{split},{krow}>",
+            f"pa_merge_balanced<{wl.head_dim},{hp}>"]
+
+
+def measure(W, pa, wl, args, stream, steps, warmup, append_steps=0, copy_calibration=False):
+    """Time pa_decode on one workload: wall clock and HIP events around `steps`
+    back-to-back calls over rotated cold copies of the K/V pools, plus single calls."""
     import numpy as np
     import torch
-
-    from decode_attention_paged_03_amd import pa
-    from decode_attention_paged_03_amd import workloads as W
-
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    torch.cuda.set_device(0)
-    pa.load()
-
-    wl = W.make_named(args.workload)
     dec = pa.decoder_for(wl, partition_size=args.partition)
     dev = "cuda"
-    stream = torch.cuda.current_stream()
-
     q = torch.from_numpy(wl.query).to(dev)
     bt = torch.from_numpy(wl.block_tables).to(dev)
     ctx = torch.from_numpy(wl.context_lengths).to(dev)
@@ -450,29 +519,26 @@ def main():
         j = i % n_copies
         dec(q, ks[j], vs[j], bt, ctx, wl.scale, out=out, stream=stream)
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record(stream)
-    for i in range(args.steps):
+    for i in range(steps):
         step(i)
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     region_ms = start.elapsed_time(end)
-
-    ms_per_step = wall / args.steps * 1e3
+    ms_per_step = wall / steps * 1e3
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
-    avg_launch_ms = region_ms / args.steps
+    avg_launch_ms = region_ms / steps
     achieved = kv_bytes / (avg_launch_ms * 1e-3) / 1e9
 
     # distribution of single calls: an event pair around each call, calls back to back
-    n_single = min(args.steps, 200)
+    n_single = min(steps, 200)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(n_single)]
     for i, (e0, e1) in enumerate(evs):
@@ -481,10 +547,10 @@ def main():
         e1.record(stream)
     torch.cuda.synchronize()
     single_us = np.array([e0.elapsed_time(e1) * 1e3 for e0, e1 in evs])
+    median_us = float(np.median(single_us))
 
-    append_line = measure_append(dec, wl, ks[0], vs[0], bt, stream, args.append_steps)
-
-    if args.copy_calibration:
+    append_line = measure_append(dec, wl, ks[0], vs[0], bt, stream, append_steps)
+    if copy_calibration:
         n = COPY_BYTES // 4
         src = torch.randn(n, device=dev)
         dst = torch.empty_like(src)
@@ -492,23 +558,17 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
 
-    traffic = traffic_per_call(wl.name) if args.partition == 0 else None
-    balanced = dec.problem.partition_size == 0 and dec.problem.flags == 0
+    balanced = dec.problem.partition_size == 0 and \
+        (dec.problem.flags & (pa.PA_FLAG_FORCE_SPLIT | pa.PA_FLAG_FORCE_SINGLE)) == 0
     kernel_name = ("pa_decode call: pa_decode_balanced + pa_merge_balanced" if balanced
                    else "pa_decode call: pa_decode_kernel (+ pa_merge_kernel when split)")
-    line = {
-        "metric": METRIC,
+    traffic = traffic_per_call(wl.name) if args.partition == 0 else None
+    res = {
         "value": round(value, 3),
         "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 6),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic",
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 3),
+        "tokens_per_s": round(wl.batch / (ms_per_step * 1e-3), 1),
         "config": {
             "workload": wl.name,
             "batch": wl.batch, "query_heads": wl.query_heads, "kv_heads": wl.kv_heads,
@@ -522,8 +582,6 @@ def main():
             "kv_pool_copies_rotated": n_copies,
             "seed": wl.seed,
         },
-        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 3),
-        "tokens_per_s": round(wl.batch / (ms_per_step * 1e-3), 1),
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 3),
@@ -534,14 +592,94 @@ def main():
             "kernel": kernel_name,
             "avg_launch_us": round(avg_launch_ms * 1e3, 3),
             "call_us_p10_median_p90": [round(float(np.percentile(single_us, q)), 3) for q in (10, 50, 90)],
-            "timing": f"HIP events on the call's stream around {args.steps} back-to-back calls",
+            "frac_single_call_median": round(kv_bytes / (median_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 5),
+            "timing": f"HIP events on the call's stream around {steps} back-to-back calls",
         },
     }
+    if balanced:
+        res["roofline"]["resources"] = kernel_resources(decode_kernel_names(dec, wl))
     if append_line:
-        line["append"] = append_line
+        res["append"] = append_line
     dec.close()
+    del ks, vs, k0, v0, q, bt, ctx, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    args = parse()
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace, args.workload))
+        return
+    if args.summarize_pmc:
+        print(summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload))
+        return
+    if args.summarize_counters:
+        print(summarize_counters(args.summarize_counters, args.workload))
+        return
+    if args.write_resources:
+        print(write_resources())
+        return
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from decode_attention_paged_03_amd import pa
+    from decode_attention_paged_03_amd import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    pa.load()
+    stream = torch.cuda.current_stream()
+
+    also = [] if args.also in ("", "none") else \
+        [w for w in args.also.split(",") if w and w != args.workload]
+    for w in also:
+        if w not in W.WORKLOADS:
+            raise SystemExit(f"bench.py: unknown workload {w!r} in --also")
+
+    wl = W.make_named(args.workload)
+    head = measure(W, pa, wl, args, stream, args.steps, args.warmup, args.append_steps,
+                   args.copy_calibration)
+    line = {
+        "metric": METRIC,
+        "value": head["value"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": head["config"],
+        "pct_hbm_peak": head["pct_hbm_peak"],
+        "tokens_per_s": head["tokens_per_s"],
+        "roofline": head["roofline"],
+    }
+    if "append" in head:
+        line["append"] = head["append"]
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    del wl
+    # the other workloads: same protocol, fewer steps, each in the "workloads" object
+    others = {}
+    for name in also:
+        wl = W.make_named(name)
+        r = measure(W, pa, wl, args, stream, min(args.steps, 200), args.warmup)
+        if not args.no_cpu_baseline:
+            big = name == "mixed128"
+            r["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds / 3.0,
+                                             modes=("all",) if big else ("single", "all"),
+                                             reps=1 if big else 3)
+        others[name] = r
+        del wl
+    if others:
+        line["workloads"] = others
     print(json.dumps(line), flush=True)
 
 

@@ -86,21 +86,28 @@ def parse_resource_usage(text: str) -> dict:
     return out
 
 
+def short_kernel_name(mangled: str) -> str:
+    """'pa_decode_balanced<128,4,1,12,0,1>' from an Itanium-mangled kernel name in this
+    library (integer and bool template arguments only)."""
+    import re
+    m = re.search(r"N_1(\d+)(pa_\w+)", mangled) or re.search(r"(\d+)(pa_\w+)", mangled)
+    if not m:
+        return mangled
+    n = int(m.group(1))
+    name = m.group(2)[:n]
+    rest = m.group(2)[n:]
+    if not rest.startswith("I"):
+        return name
+    args = re.findall(r"L[ib](\d+)E", rest[:rest.find("EE") + 2] if "EE" in rest else rest)
+    return f"{name}<{','.join(args)}>"
+
+
 def resource_table(text: str) -> str:
     """One line per kernel: registers, scratch, occupancy and LDS."""
-    import re
-    rows = []
-    for name, f in parse_resource_usage(text).items():
-        m = re.search(r"(pa_\w+?)(I.*)?E?vNS0_|(pa_\w+)", name)
-        short = name
-        dm = re.search(r"N_1\d+(pa_[a-z_]+)(I[^E]*(?:E[^v]*)?)?", name)
-        if dm:
-            short = dm.group(1) + "<" + ",".join(re.findall(r"Li(\d+)E|Lb(\d)E", name and dm.group(2) or "") and
-                                               [a or b for a, b in re.findall(r"Li(\d+)E|Lb(\d)E", dm.group(2) or "")]) + ">"
-        rows.append((short, f))
+    rows = sorted((short_kernel_name(name), f) for name, f in parse_resource_usage(text).items())
     cols = [key for _, key in _FIELDS]
     lines = [f"{'kernel':<40} " + " ".join(f"{c:>10}" for c in cols)]
-    for short, f in sorted(rows):
+    for short, f in rows:
         lines.append(f"{short:<40} " + " ".join(f"{f.get(c, -1):>10}" for c in cols))
     return "\n".join(lines)
 

@@ -69,3 +69,48 @@ def test_counter_summary_without_values_fails(tmp_path, monkeypatch):
     (tmp_path / "empty").mkdir()
     with pytest.raises(SystemExit):
         bench.summarize_counters([str(tmp_path / "empty")], "w")
+
+
+def test_resources_keyed_by_kernel_hash(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    rows = ("kernel  sgpr vgpr agpr scratch waves/simd sgpr_spill vgpr_spill lds\n"
+            "pa_decode_balanced<128,4,1,12,0,1> 106 149 0 0 3 25 0 105664\n")
+    (tmp_path / "resources.txt").write_text("kernel_source_sha256: 0000\n" + rows)
+    assert bench.kernel_resources(["pa_decode_balanced<128,4,1,12,0,1>"]) is None
+    (tmp_path / "resources.txt").write_text(f"kernel_source_sha256: {bench.kernel_source_hash()}\n" + rows)
+    got = bench.kernel_resources(["pa_decode_balanced<128,4,1,12,0,1>", "absent<1>"])
+    assert got == {"pa_decode_balanced<128,4,1,12,0,1>": dict(sgpr=106, vgpr=149, agpr=0, scratch=0,
+                                                                **{"waves/simd": 3}, sgpr_spill=25,
+                                                                vgpr_spill=0, lds=105664)}
+
+
+def test_committed_resources_cover_the_benched_kernels():
+    """profiles/resources.txt exists, and when it matches the current sources it lists
+    the kernels the bench reports for each workload."""
+    from decode_attention_paged_03_amd import workloads as W
+    path = os.path.join(ROOT, "profiles", "resources.txt")
+    assert os.path.exists(path)
+    text = open(path).read()
+    if f"kernel_source_sha256: {bench.kernel_source_hash()}" not in text:
+        pytest.skip("resources.txt predates the current kernel sources")
+    for name, spec in W.WORKLOADS.items():
+        class _Wl:
+            group = spec["query_heads"] // spec["kv_heads"]
+            page_size = spec["page_size"]
+            head_dim = spec["head_dim"]
+        names = bench.decode_kernel_names(None, _Wl)
+        assert bench.kernel_resources(names) is not None and len(bench.kernel_resources(names)) == 2, name
+
+
+def test_cpu_baseline_fields():
+    """Single-thread and all-thread oracle runs, the thread counts used and the host's
+    core count reported separately."""
+    from decode_attention_paged_03_amd import workloads as W
+    wl = W.make_named("tiny")
+    line = bench.cpu_baseline(wl, 0.05, reps=2)
+    assert line["kind"] == "oracle" and line["unit"] == "GB/s" and line["value"] > 0
+    assert line["single"]["threads"] == 1
+    assert line["all"]["threads"] == line["cores"] == min(bench.host_cores(), bench.CPU_SHARE)
+    assert line["host_cores"] == bench.host_cores()
+    assert line["single"]["evaluations"] == 2
+    assert "output rows" in line["sample"]
