@@ -54,7 +54,8 @@ int build_plan(const pa_problem* in, Plan* pl) {
         p.max_context_length < 0)
         return PA_ERR_INVALID_ARGUMENT;
     if (p.query_heads % p.kv_heads) return PA_ERR_INVALID_ARGUMENT;
-    const uint32_t known = PA_FLAG_FORCE_SPLIT | PA_FLAG_FORCE_SINGLE | PA_FLAG_DEBUG_BOUNDS;
+    const uint32_t known = PA_FLAG_FORCE_SPLIT | PA_FLAG_FORCE_SINGLE | PA_FLAG_DEBUG_BOUNDS |
+                           PA_FLAG_SINGLE_LAUNCH;
     if (p.flags & ~known) return PA_ERR_INVALID_ARGUMENT;
     if ((p.flags & PA_FLAG_FORCE_SPLIT) && (p.flags & PA_FLAG_FORCE_SINGLE))
         return PA_ERR_INVALID_ARGUMENT;
@@ -82,6 +83,10 @@ int build_plan(const pa_problem* in, Plan* pl) {
     out.balanced = p.partition_size == 0 && route_flags == 0 && p.batch <= kMaxBalancedBatch &&
                    max_tiles <= INT32_MAX;
     out.debug_bounds = (p.flags & PA_FLAG_DEBUG_BOUNDS) != 0;
+    out.single_launch = (p.flags & PA_FLAG_SINGLE_LAUNCH) != 0;
+    // one launch needs the default route: no partition size, no route flag
+    if (out.single_launch && (p.partition_size != 0 || route_flags != 0)) return PA_ERR_INVALID_ARGUMENT;
+    if (out.single_launch && !out.balanced) return PA_ERR_UNSUPPORTED;
     // the bitmap has one bit per table entry
     if (out.debug_bounds && (long long)p.batch * p.max_pages_per_sequence > (1LL << 40))
         return PA_ERR_UNSUPPORTED;
@@ -133,13 +138,13 @@ int build_plan(const pa_problem* in, Plan* pl) {
 }
 
 WsLayout workspace_layout(const Plan& pl, int wg_slots) {
-    WsLayout l{0, 0, 0, 0, 0, wg_slots};
+    WsLayout l{0, 0, 0, 0, 0, 0, wg_slots};
     if (pl.debug_bounds) {
         l.bitmap_words = ((size_t)pl.prob.batch * (size_t)pl.prob.max_pages_per_sequence + 31) / 32;
         l.acc_offset = (l.bitmap_words * 4 + 255) / 256 * 256;
     }
     if (!pl.need_merge) {
-        l.ml_offset = l.desc_offset = l.bytes = l.acc_offset;
+        l.ml_offset = l.desc_offset = l.cnt_offset = l.bytes = l.acc_offset;
         return l;
     }
     size_t rows;
@@ -154,7 +159,8 @@ WsLayout workspace_layout(const Plan& pl, int wg_slots) {
     }
     l.ml_offset = l.acc_offset + rows * (size_t)pl.prob.head_dim * sizeof(float);
     l.desc_offset = l.ml_offset + rows * 2 * sizeof(float);
-    l.bytes = l.desc_offset + (pl.balanced ? (size_t)wg_slots * 2 * 16 : 0);
+    l.cnt_offset = l.desc_offset + (pl.balanced ? (size_t)wg_slots * 2 * 16 : 0);
+    l.bytes = l.cnt_offset + (pl.single_launch ? (size_t)wg_slots * 3 * sizeof(int) : 0);
     l.wg_slots = wg_slots;
     return l;
 }
@@ -232,13 +238,20 @@ pa_status pa_decode_noalloc(const pa_handle* handle, const void* query, const vo
     const pa::Plan& pl = handle->plan;
     if (pl.debug_bounds) return PA_ERR_INVALID_ARGUMENT;   // its bitmap needs a caller workspace
     void* scratch = nullptr;
-    pa::WsLayout layout{0, 0, 0, 0, 0, 0};
+    pa::WsLayout layout{0, 0, 0, 0, 0, 0, 0};
     if (pl.need_merge) {
         // the balanced route's rows are indexed by workgroup: sized for this device's grid
         const int slots = pl.balanced ? pa::device_compute_units() : 0;
         if (pl.balanced && slots <= 0) return PA_ERR_HIP;
         layout = pa::workspace_layout(pl, slots);
-        if (layout.bytes > pa::kNoallocScratchBytes) return PA_ERR_SCRATCH;
+        // the scratch's tail holds the single-launch counters, which no layout may reach
+        const size_t usable = pa::kNoallocScratchBytes - pa::kNoallocCounterBytes;
+        if (layout.cnt_offset > usable) return PA_ERR_SCRATCH;
+        if ((size_t)slots * 3 * sizeof(int) > pa::kNoallocCounterBytes) return PA_ERR_SCRATCH;
+        if (pl.single_launch) {
+            layout.cnt_offset = usable;
+            layout.bytes = pa::kNoallocScratchBytes;
+        }
         size_t cap = 0;
         if (!pa::noalloc_scratch(&scratch, &cap)) return PA_ERR_HIP;
         if (layout.bytes > cap) return PA_ERR_SCRATCH;

@@ -26,6 +26,9 @@ constexpr int kMaxBalancedWG = 1024;
 // (2 sides x 12 streams x 8 heads of 520-byte rows per workgroup, plus its records), and for
 // fixed partitions up to that size.
 constexpr size_t kNoallocScratchBytes = (size_t)PA_NOALLOC_SCRATCH_BYTES;
+// The scratch's last bytes: single-launch arrival counters (3 ints per workgroup), zero from
+// load time on because no other layout reaches them and every call leaves them at zero.
+constexpr size_t kNoallocCounterBytes = 64 * 1024;
 // Query heads one wave scores at once (MFMA rows are 16; LDS partial slots are sized
 // for this many heads).
 constexpr int kMaxHeadsPerWave = 8;
@@ -48,6 +51,7 @@ struct Plan {
     int ps_log2;            // log2(page_size)
     bool need_merge;        // a merge kernel is launched
     bool debug_bounds;      // PA_FLAG_DEBUG_BOUNDS: record table entries outside the pool
+    bool single_launch;     // PA_FLAG_SINGLE_LAUNCH: the decode kernel merges crossing bands
     size_t rows_per_wg;     // balanced route: partial rows per workgroup (2 sides x spw x heads)
     size_t ws_bytes;        // workspace bytes pa_workspace_size() reports (0 when need_merge is
                             // false): the layout for kMaxBalancedWG workgroups
@@ -65,6 +69,7 @@ struct WsLayout {
     size_t acc_offset;      // byte offset of the partial rows (the bitmap rounded to 256 B)
     size_t ml_offset;       // byte offset of the (max, sum) pairs
     size_t desc_offset;     // balanced route: byte offset of the per-workgroup merge records
+    size_t cnt_offset;      // single launch: byte offset of the arrival counters (3 per workgroup)
     size_t bytes;           // total (0 when no merge is launched and no bitmap is kept)
     int wg_slots;           // balanced route: workgroups the partial rows are sized for
 };

@@ -113,6 +113,8 @@ struct DecodeArgs {
     float* ws_acc;          // partial rows of D floats
     float* ws_ml;           // partial rows' (max in log2 units, sum)
     int4* ws_desc;          // balanced route: two merge records per workgroup
+    int* ws_cnt;            // single launch: band counters [grid], then group counters [2 grid]
+    int single_launch;      // balanced route: the decode kernel merges crossing bands itself
     float scale_log2;       // |scale| * log2(e)
     uint32_t q_sign;        // 0x80008000 to negate q (negative scale), else 0
     int batch, query_heads, kv_heads, group, n_chunks, max_pages, partition, n_part_max, ps_log2;
@@ -867,6 +869,182 @@ __device__ __forceinline__ int wg_of_unit(int c, int N, int W) {
     return min(x, W - 1);
 }
 
+// Single launch (PA_FLAG_SINGLE_LAUNCH): the workgroups of a crossing band merge it
+// themselves, at the end of the decode kernel, instead of a second kernel -- the
+// "last-arriving workgroup merges" form of the split/merge of the "V4 (Context-axis
+// parallelism)" section of "[TIL] Optimizing paged attention".
+//
+// Workgroup x holds a piece of at most two crossing bands (records: the band holding its
+// first unit, started in an earlier workgroup o -- piece on side 0; the band it owns --
+// piece on the records' side).  A band owned by o has participants o .. o + n - 1, in
+// groups of kArrivalGroup from the owner: group g has leader L = o + kArrivalGroup g.
+// Each participant, once its pieces are in memory, increments its group's counter (group
+// counter slot 2 L + 1 when L is the owner, else 2 L); the one that sees the group's
+// size - 1 folds the group's pieces (in participant order) into the leader's piece slot,
+// or straight into the output when the band has one group, and resets the counter.  With
+// several groups, each group merger then increments the band counter (slot o); the one
+// that sees the group count - 1 folds the group triples into the output and resets it.
+// So no workgroup folds more than kArrivalGroup triples, and every counter is zero again
+// when the kernel ends (the caller zeroes them once, before the first call).
+// Arrivals are release atomics at device scope (the pieces are written back from this
+// XCD's L2 first); a merger's acquire invalidates its caches before it reads.
+constexpr int kArrivalGroup = 16;
+
+// Fold np (<= NP) triples of every row of a band, in order p = 0 .. np - 1: triple p of row
+// r is workspace row src(p) + r.  The result goes to workspace rows dst + r (unnormalised,
+// when to_out is false) or to the band's output rows.  Every load of a task is issued
+// before any is used; lanes past np reload triple 0 and weigh nothing.
+template <int D, int HP, int NP, typename Src>
+__device__ __forceinline__ void fold_band(const DecodeArgs& a, int spw, int np, Src src, bool to_out,
+                                          size_t dst, int b, int band, int nthreads) {
+    constexpr int C4 = D / 4;
+    const int rows = spw * HP;
+    for (int task = threadIdx.x; task < rows * C4; task += nthreads) {
+        const int r = task / C4;
+        const int c4 = task - r * C4;
+        float4_t pa[NP];
+        float pm[NP], pl[NP];
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const size_t row = src(p < np ? p : 0) + r;
+            pa[p] = reinterpret_cast<const float4_t*>(a.ws_acc + row * D)[c4];
+            pm[p] = a.ws_ml[row * 2];
+            pl[p] = a.ws_ml[row * 2 + 1];
+        }
+        float M = -INFINITY;
+#pragma unroll
+        for (int p = 0; p < NP; ++p) M = fmaxf(M, p < np ? pm[p] : -INFINITY);
+        const float Ms = M == -INFINITY ? 0.f : M;   // a group of empty workgroups: weight 0
+        float L = 0.f;
+        float4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const float e = p < np ? fast_exp2(pm[p] - Ms) : 0.f;
+            L += e * pl[p];
+            acc += e * pa[p];
+        }
+        if (to_out) {
+            const int sp = r / HP;
+            const int h = r - sp * HP;
+            const int s = band * spw + sp;
+            const int kvh = s / a.n_chunks;
+            const int chunk = s - kvh * a.n_chunks;
+            reinterpret_cast<float4_t*>(a.out + ((size_t)b * a.query_heads + kvh * a.group + chunk * HP + h) * D)[c4] = acc / L;
+        } else {
+            reinterpret_cast<float4_t*>(a.ws_acc + (dst + r) * D)[c4] = acc;
+            if (c4 == 0) {
+                a.ws_ml[(dst + r) * 2] = M;
+                a.ws_ml[(dst + r) * 2 + 1] = L;
+            }
+        }
+    }
+}
+
+template <int D, int HP, typename Src>
+__device__ __forceinline__ void fold_band_n(const DecodeArgs& a, int spw, int np, Src src, bool to_out,
+                                            size_t dst, int b, int band, int nthreads) {
+    static_assert(kArrivalGroup == 16, "fold shapes below cover up to 16 triples");
+    if (np <= 4) fold_band<D, HP, 4>(a, spw, np, src, to_out, dst, b, band, nthreads);
+    else if (np <= 8) fold_band<D, HP, 8>(a, spw, np, src, to_out, dst, b, band, nthreads);
+    else fold_band<D, HP, 16>(a, spw, np, src, to_out, dst, b, band, nthreads);
+}
+
+// The arrivals of one thread on up to two counters (release once, then both atomics in
+// flight together): bit t of the result says whether the caller was the last of
+// expected[t] on counter[t] (then with an acquire done and that counter reset).
+__device__ __forceinline__ int arrive_last2(int* const (&counter)[2], const int (&expected)[2]) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    int old[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+        old[t] = counter[t] ? __hip_atomic_fetch_add(counter[t], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : -1;
+    int last = 0;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+        if (counter[t] && old[t] == expected[t] - 1) last |= 1 << t;
+    if (last) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+            if (last & (1 << t)) __hip_atomic_store(counter[t], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return last;
+}
+
+template <int D, int HP, int NT>
+__device__ __forceinline__ void single_launch_merge(const DecodeArgs& a, int w, int NWG, int spw,
+                                                    const int4 (&s_rec)[2], int (&s_last)[4]) {
+    const size_t rows = (size_t)spw * HP;
+    auto slot = [&](int x, int side) { return ((size_t)x * 2 + side) * rows; };
+    int* band_cnt = a.ws_cnt;
+    int* grp_cnt = a.ws_cnt + NWG;
+    // band t (0: the covering band, 1: the own band): owner, pieces, owner's side, group
+    int n[2], o[2], side_o[2], L[2], sg[2], ng[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int4 r = s_rec[t == 0 ? 1 : 0];
+        n[t] = t == 0 ? r.w : r.z;
+        o[t] = t == 0 ? (r.z >> 1) : w;
+        side_o[t] = t == 0 ? (r.z & 1) : r.w;
+        const int g = n[t] > 0 ? (w - o[t]) / kArrivalGroup : 0;
+        L[t] = o[t] + kArrivalGroup * g;
+        sg[t] = min(kArrivalGroup, n[t] - kArrivalGroup * g);
+        ng[t] = (n[t] + kArrivalGroup - 1) / kArrivalGroup;
+    }
+    if (n[0] <= 0 && n[1] <= 0) return;              // block-uniform: no crossing band
+    // this wave's piece stores have reached L2 (the counter counts stores on this target);
+    // after the barrier, every piece of this workgroup has
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int* c[2];
+        int e[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            c[t] = n[t] > 0 ? grp_cnt + 2 * L[t] + (L[t] == o[t] ? 1 : 0) : nullptr;
+            e[t] = sg[t];
+        }
+        s_last[0] = arrive_last2(c, e);
+    }
+    __syncthreads();
+    const int last1 = s_last[0];
+    int need2 = 0;                                    // bands whose group triple needs a band merge
+    for (int t = 0; t < 2; ++t) {
+        if (!(last1 & (1 << t))) continue;            // block-uniform
+        const int4 r = s_rec[t == 0 ? 1 : 0];
+        const int ot = o[t], st = side_o[t], Lt = L[t];
+        fold_band_n<D, HP>(a, spw, sg[t], [&](int p) { return slot(Lt + p, Lt + p == ot ? st : 0); },
+                           ng[t] == 1, slot(Lt, Lt == ot ? st : 0), r.x, r.y, NT);
+        if (ng[t] > 1) need2 |= 1 << t;
+    }
+    if (!need2) return;                               // block-uniform
+    __builtin_amdgcn_s_waitcnt(0);                    // the group triples have reached L2
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int* c[2];
+        int e[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            c[t] = (need2 & (1 << t)) ? band_cnt + o[t] : nullptr;
+            e[t] = ng[t];
+        }
+        s_last[1] = arrive_last2(c, e);
+    }
+    __syncthreads();
+    const int last2 = s_last[1];
+    for (int t = 0; t < 2; ++t) {
+        if (!(last2 & (1 << t))) continue;
+        const int4 r = s_rec[t == 0 ? 1 : 0];
+        const int ot = o[t], st = side_o[t];
+        fold_band_n<D, HP>(a, spw, ng[t],
+                           [&](int p) {
+                               const int Lg = ot + kArrivalGroup * p;
+                               return slot(Lg, Lg == ot ? st : 0);
+                           },
+                           true, 0, r.x, r.y, NT);
+    }
+}
+
 template <int D, int HP, int DEPTH, int NW, bool SPLIT, bool KROW>
 __global__ void __launch_bounds__(NW * 64)
 pa_decode_balanced(DecodeArgs a) {
@@ -885,6 +1063,8 @@ pa_decode_balanced(DecodeArgs a) {
     __shared__ int s_meta[NS][3];    // stream id (-1: empty), first unit, end unit
     __shared__ int s_runs[NS + 1];   // first slot of each run of one stream's slots, then NS
     __shared__ int s_nruns;
+    __shared__ int4 s_rec[2];        // the workgroup's merge records (own band, covering band)
+    __shared__ int s_last[4];        // single launch: whether this workgroup merges (per stage)
     __shared__ uint4 s_kt[KROW ? NW * 16 * kKtStride : 1];   // whole-row K staging, per wave
 
     const int B = a.batch;
@@ -1122,6 +1302,8 @@ pa_decode_balanced(DecodeArgs a) {
         }
         a.ws_desc[2 * w] = own;
         a.ws_desc[2 * w + 1] = cov;
+        s_rec[0] = own;
+        s_rec[1] = cov;
     };
     if (nk > 0) {
         // DEPTH register buffers: tile i + DEPTH - 1 is loaded before tile i is consumed.
@@ -1305,7 +1487,7 @@ pa_decode_balanced(DecodeArgs a) {
             }
         }
     }
-
+    if (a.single_launch) single_launch_merge<D, HP, NT>(a, w, NWG, SPW, s_rec, s_last);
 }
 
 // Merge of the balanced route.  Workgroup w of the decode kernel owns the band that
@@ -1624,7 +1806,7 @@ hipError_t launch_balanced_nw(const Plan& pl, const DecodeArgs& args, int ws_slo
     if (grid > ws_slots) return hipErrorInvalidValue;   // the workspace holds fewer workgroups' rows
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NW * 64), lds, stream, args);
     hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
+    if (err != hipSuccess || args.single_launch) return err;
     hipLaunchKernelGGL((pa_merge_balanced<D, HP>), dim3((unsigned)grid), dim3(kMergeThreads), 0, stream, args);
     return hipGetLastError();
 }
@@ -1706,6 +1888,8 @@ hipError_t launch(const Plan& pl, const void* q, const void* k, const void* v,
         ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + layout.ml_offset);
         if (pl.balanced) ws_desc = reinterpret_cast<int4*>(static_cast<char*>(workspace) + layout.desc_offset);
     }
+    int* ws_cnt = pl.single_launch ? reinterpret_cast<int*>(static_cast<char*>(workspace) + layout.cnt_offset)
+                                   : nullptr;
     if (pl.debug_bounds) {
         const long long words = (long long)layout.bitmap_words;
         hipLaunchKernelGGL(pa_bad_entries_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, stream,
@@ -1725,6 +1909,8 @@ hipError_t launch(const Plan& pl, const void* q, const void* k, const void* v,
     da.ws_acc = ws_acc;
     da.ws_ml = ws_ml;
     da.ws_desc = ws_desc;
+    da.ws_cnt = ws_cnt;
+    da.single_launch = pl.single_launch ? 1 : 0;
     da.scale_log2 = fabsf(scale) * kLog2e;
     da.q_sign = scale < 0.f ? 0x80008000u : 0u;
     da.batch = p.batch;

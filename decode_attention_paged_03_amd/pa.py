@@ -30,6 +30,7 @@ PA_NOALLOC_SCRATCH_BYTES = 32 << 20
 PA_FLAG_FORCE_SPLIT = 0x1
 PA_FLAG_FORCE_SINGLE = 0x2
 PA_FLAG_DEBUG_BOUNDS = 0x4
+PA_FLAG_SINGLE_LAUNCH = 0x8
 
 EXPORTED = ("pa_create", "pa_workspace_size", "pa_decode", "pa_decode_noalloc", "pa_append",
             "pa_destroy", "pa_status_string")
@@ -145,7 +146,10 @@ class PagedDecoder:
         self.problem = problem
         self.handle = pa_create(problem)
         self.workspace_bytes = pa_workspace_size(self.handle)
-        self.workspace = (torch.empty(self.workspace_bytes, dtype=torch.uint8, device=device)
+        # PA_FLAG_SINGLE_LAUNCH keeps arrival counters in the workspace, zero before the first
+        # call (every call leaves them at zero)
+        alloc = torch.zeros if problem.flags & PA_FLAG_SINGLE_LAUNCH else torch.empty
+        self.workspace = (alloc(self.workspace_bytes, dtype=torch.uint8, device=device)
                           if self.workspace_bytes else None)
 
     def __call__(self, query, key_cache, value_cache, block_tables, context_lengths, scale,

@@ -65,7 +65,8 @@ typedef enum pa_status {
 } pa_status;
 
 /* Bytes of the device scratch array pa_decode_noalloc() uses in place of a workspace (one
- * array per GPU, held until the process ends). */
+ * array per GPU, held until the process ends).  Its last 64 KiB hold the arrival counters
+ * of PA_FLAG_SINGLE_LAUNCH calls; a problem's workspace must fit in the rest. */
 #define PA_NOALLOC_SCRATCH_BYTES (32u << 20)
 
 /* Flags for pa_problem.flags */
@@ -83,6 +84,18 @@ typedef enum pa_status {
  * words after the stream passes the call.  pa_workspace_size() includes them, rounded up
  * to 256 bytes. */
 #define PA_FLAG_DEBUG_BOUNDS 0x4u
+/* One kernel launch per call on the default route: the workgroups that share a context
+ * split merge it themselves at the end of the decode kernel (the last to arrive on a
+ * counter merges; long splits in two levels of at most 16 pieces each) instead of a
+ * second merge kernel, the split and merge of the first page's "V4 (Context-axis
+ * parallelism)" section in one launch.  Only without a partition size or the route flags
+ * above.  The workspace then ends with arrival counters that must be zero before the
+ * first call: zero the whole workspace once after allocating it (e.g. hipMemset), and
+ * again after using it for any other problem or route.  Every call leaves its counters
+ * at zero.  (pa_decode_noalloc keeps its own counters, zero from the start.)  Measured
+ * slower than the two launches on the serving-shaped and long-context workloads: the
+ * device-scope arrivals cost more than the second launch. */
+#define PA_FLAG_SINGLE_LAUNCH 0x8u
 
 typedef struct pa_problem {
     int32_t batch;                  /* number of sequences, >= 1                                  */

@@ -76,9 +76,15 @@ def create_status(prob):
     (dict(partition_size=16 * 513), pa.PA_ERR_UNSUPPORTED),
     (dict(max_context_length=8 * 16 + 1), pa.PA_ERR_INVALID_ARGUMENT),
     (dict(flags=0x100), pa.PA_ERR_INVALID_ARGUMENT),
-    (dict(flags=0x8), pa.PA_ERR_INVALID_ARGUMENT),
+    (dict(flags=0x10), pa.PA_ERR_INVALID_ARGUMENT),
     (dict(flags=pa.PA_FLAG_DEBUG_BOUNDS), pa.PA_OK),
     (dict(flags=pa.PA_FLAG_DEBUG_BOUNDS | pa.PA_FLAG_FORCE_SPLIT), pa.PA_OK),
+    (dict(flags=pa.PA_FLAG_SINGLE_LAUNCH), pa.PA_OK),
+    (dict(flags=pa.PA_FLAG_SINGLE_LAUNCH | pa.PA_FLAG_DEBUG_BOUNDS), pa.PA_OK),
+    (dict(flags=pa.PA_FLAG_SINGLE_LAUNCH, partition_size=16), pa.PA_ERR_INVALID_ARGUMENT),
+    (dict(flags=pa.PA_FLAG_SINGLE_LAUNCH | pa.PA_FLAG_FORCE_SPLIT), pa.PA_ERR_INVALID_ARGUMENT),
+    (dict(flags=pa.PA_FLAG_SINGLE_LAUNCH, batch=4096, max_pages_per_sequence=1,
+          num_physical_pages=4096), pa.PA_ERR_UNSUPPORTED),
     (dict(flags=pa.PA_FLAG_FORCE_SPLIT | pa.PA_FLAG_FORCE_SINGLE), pa.PA_ERR_INVALID_ARGUMENT),
     (dict(flags=pa.PA_FLAG_FORCE_SINGLE, max_pages_per_sequence=4096), pa.PA_ERR_UNSUPPORTED),
 ])
@@ -124,6 +130,13 @@ def test_workspace_size():
     assert ws_size(partition_size=1024) == 0
     assert ws_size(flags=pa.PA_FLAG_FORCE_SPLIT) == 2 * 8 * 1 * (128 + 2) * 4
     assert ws_size(flags=pa.PA_FLAG_FORCE_SINGLE, max_pages_per_sequence=64) == 0
+
+
+def test_workspace_size_single_launch():
+    # PA_FLAG_SINGLE_LAUNCH adds three arrival counters per workgroup slot at the end
+    assert ws_size(flags=pa.PA_FLAG_SINGLE_LAUNCH) == ws_size() + 1024 * 3 * 4
+    assert ws_size(flags=pa.PA_FLAG_SINGLE_LAUNCH | pa.PA_FLAG_DEBUG_BOUNDS) == \
+        256 + ws_size() + 1024 * 3 * 4
 
 
 def test_workspace_size_with_bounds_bitmap():

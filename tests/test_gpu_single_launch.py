@@ -1,0 +1,97 @@
+"""PA_FLAG_SINGLE_LAUNCH: one kernel per call, the workgroups of a crossing band merging it
+themselves (last arrival on a counter; bands of more than 16 pieces in two levels).
+Checked against the oracle (|gpu - oracle| <= 1e-3 * (1 + |oracle|)) on the workloads and
+on band spans of 2 to 128 pieces; repeated calls are bitwise equal and leave every arrival
+counter at zero (the protocol's own reset); the no-allocation entry point gives the same
+bits."""
+import numpy as np
+import pytest
+
+from decode_attention_paged_03_amd import pa
+from decode_attention_paged_03_amd import workloads as W
+
+import gpu_common as C
+
+pytestmark = pytest.mark.gpu
+
+SL = pa.PA_FLAG_SINGLE_LAUNCH
+COUNTER_BYTES = 3 * 1024 * 4      # the workspace's last bytes: counters for 1024 workgroups
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    pa.load()
+    yield
+
+
+def _run_checked(wl, what, repeats=3):
+    import torch
+    C.say(f"[case] single launch {what}: {wl.summary()}")
+    dev = C.Device(wl)
+    dec = pa.decoder_for(wl, partition_size=0, flags=SL)
+    try:
+        outs = []
+        for _ in range(repeats):
+            outs.append(dev.run(dec).clone())
+            cnt = dec.workspace[-COUNTER_BYTES:].cpu().numpy().view(np.int32)
+            assert not cnt.any(), f"{what}: arrival counters left non-zero: {np.flatnonzero(cnt)[:8]}"
+        for o in outs[1:]:
+            assert torch.equal(outs[0].view(torch.int32), o.view(torch.int32)), f"{what}: calls differ"
+        ref = C.oracle.attend_workload(wl, nthreads=C.oracle_threads())
+        C.check_against_oracle(outs[0].cpu().numpy(), ref, f"single launch {what}")
+        return outs[0]
+    finally:
+        dec.close()
+
+
+@pytest.mark.parametrize("name", ["tiny", "small_batch", "batch64", "long100k", "mixed128"])
+def test_workloads(name):
+    _run_checked(W.make_named(name), name)
+
+
+SPANS = [
+    # (label, contexts, query heads, kv heads): spans of a few pieces to two-level bands
+    ("short spans", [700, 2100, 33, 1500, 5000, 40, 900, 1], 16, 4),
+    ("one long sequence among short ones", [60000, 9, 300, 17], 24, 4),
+    ("mha long", [3000, 20000], 8, 8),
+    ("mqa", [1, 15, 16, 17, 4000], 8, 1),
+    ("empty and tiny", [0, 1, 0, 2, 3], 16, 2),
+]
+
+
+@pytest.mark.parametrize("case", SPANS, ids=lambda c: c[0])
+def test_band_spans(case):
+    label, ctx, qh, kvh = case
+    wl = W.make_workload(name="sl", batch=len(ctx), query_heads=qh, kv_heads=kvh, head_dim=128,
+                         page_size=16, context_lengths=ctx, pool="holes10",
+                         seed=7800 + SPANS.index(case))
+    _run_checked(wl, label)
+
+
+def test_page8_and_head_dim_64():
+    wl = W.make_workload(name="sl8", batch=3, query_heads=12, kv_heads=2, head_dim=64, page_size=8,
+                         context_lengths=[7000, 5, 1031], pool="holes10", seed=7850)
+    _run_checked(wl, "pages of 8, head_dim 64")
+
+
+def test_noalloc_same_bits():
+    """pa_decode_noalloc with the flag: the scratch's own counters, the same bits as
+    pa_decode with a caller workspace, over two calls in a row."""
+    import torch
+    for name in ("batch64", "long100k"):
+        wl = W.make_named(name)
+        dev = C.Device(wl)
+        dec = pa.decoder_for(wl, partition_size=0, flags=SL)
+        try:
+            ref = dev.run(dec).clone()
+            for _ in range(2):
+                out = torch.full_like(ref, float("nan"))
+                pa.pa_decode_noalloc(dec.handle, dev.q.data_ptr(), dev.k.data_ptr(), dev.v.data_ptr(),
+                                     dev.bt.data_ptr(), dev.ctx.data_ptr(), wl.scale, out.data_ptr(), 0)
+                torch.cuda.synchronize()
+                assert torch.equal(ref.view(torch.int32), out.view(torch.int32)), name
+        finally:
+            dec.close()
