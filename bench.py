@@ -47,7 +47,10 @@ def parse():
     ap.add_argument("--workload", default="batch64",
                     choices=["tiny", "small_batch", "batch64", "long100k", "mixed128"])
     ap.add_argument("--partition", type=int, default=0,
-                    help="tokens per fixed partition (default 0: the library splits the work)")
+                    help="partition_size: no partial covers more tokens (default 0: the library "
+                         "splits the work; the library keeps its own split when that bound holds)")
+    ap.add_argument("--fixed-partitions", action="store_true",
+                    help="with --partition: partitions of exactly that size (PA_FLAG_FIXED_PARTITIONS)")
     ap.add_argument("--rotate-bytes", type=float, default=768e6,
                     help="total K/V bytes to rotate over (cold-cache timing); 0 = one copy")
     ap.add_argument("--append-steps", type=int, default=200,
@@ -499,7 +502,9 @@ def measure(W, pa, wl, args, stream, steps, warmup, append_steps=0, copy_calibra
     back-to-back calls over rotated cold copies of the K/V pools, plus single calls."""
     import numpy as np
     import torch
-    dec = pa.decoder_for(wl, partition_size=args.partition)
+    fixed = bool(args.partition and args.fixed_partitions)
+    dec = pa.decoder_for(wl, partition_size=args.partition,
+                         flags=pa.PA_FLAG_FIXED_PARTITIONS if fixed else 0)
     dev = "cuda"
     q = torch.from_numpy(wl.query).to(dev)
     bt = torch.from_numpy(wl.block_tables).to(dev)
@@ -558,10 +563,14 @@ def measure(W, pa, wl, args, stream, steps, warmup, append_steps=0, copy_calibra
             dst.copy_(src)
         torch.cuda.synchronize()
 
-    balanced = dec.problem.partition_size == 0 and \
-        (dec.problem.flags & (pa.PA_FLAG_FORCE_SPLIT | pa.PA_FLAG_FORCE_SINGLE)) == 0
-    kernel_name = ("pa_decode call: pa_decode_balanced + pa_merge_balanced" if balanced
-                   else "pa_decode call: pa_decode_kernel (+ pa_merge_kernel when split)")
+    balanced = dec.problem.partition_size == 0
+    if balanced:
+        kernel_name = "pa_decode call: pa_decode_balanced + pa_merge_balanced"
+    elif fixed:
+        kernel_name = "pa_decode call: pa_decode_kernel (+ pa_merge_kernel when split)"
+    else:
+        kernel_name = (f"pa_decode call with partition_size {args.partition}: the balanced kernels "
+                       "when their partials fit it, else pa_decode_kernel + pa_merge_kernel")
     traffic = traffic_per_call(wl.name) if args.partition == 0 else None
     res = {
         "value": round(value, 3),
@@ -577,6 +586,7 @@ def measure(W, pa, wl, args, stream, steps, warmup, append_steps=0, copy_calibra
                                 "max": int(wl.context_lengths.max()),
                                 "sum": int(wl.context_lengths.astype(np.int64).sum())},
             "partition_size": dec.problem.partition_size or "library default",
+            "fixed_partitions": fixed,
             "kv_dtype": "f16", "out_dtype": "f32",
             "kv_bytes_per_step": kv_bytes,
             "kv_pool_copies_rotated": n_copies,

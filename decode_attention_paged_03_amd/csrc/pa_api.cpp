@@ -55,7 +55,7 @@ int build_plan(const pa_problem* in, Plan* pl) {
         return PA_ERR_INVALID_ARGUMENT;
     if (p.query_heads % p.kv_heads) return PA_ERR_INVALID_ARGUMENT;
     const uint32_t known = PA_FLAG_FORCE_SPLIT | PA_FLAG_FORCE_SINGLE | PA_FLAG_DEBUG_BOUNDS |
-                           PA_FLAG_SINGLE_LAUNCH;
+                           PA_FLAG_SINGLE_LAUNCH | PA_FLAG_FIXED_PARTITIONS;
     if (p.flags & ~known) return PA_ERR_INVALID_ARGUMENT;
     if ((p.flags & PA_FLAG_FORCE_SPLIT) && (p.flags & PA_FLAG_FORCE_SINGLE))
         return PA_ERR_INVALID_ARGUMENT;
@@ -75,13 +75,17 @@ int build_plan(const pa_problem* in, Plan* pl) {
     out.n_chunks = out.group / out.heads_per_wg;
     out.ps_log2 = ilog2(p.page_size);
     // No partition size and no flag: the library splits the work itself (balanced
-    // route).  A partition size or a flag asks for fixed partitions.
-    // Its tile indices are 32-bit: all (sequence, KV head, chunk) streams together hold
-    // fewer than 2^31 tiles of 16 tokens.
+    // route).  A route flag asks for fixed partitions.  A partition size bounds the tokens
+    // any partial (max, sum, acc) triple covers: the balanced route runs when the
+    // problem's sizes guarantee its partials stay within it (decided per call, from the
+    // device's compute units; see balanced_partials_fit), else fixed partitions of exactly
+    // that size.  The balanced route's tile indices are 32-bit: all (sequence, KV head,
+    // chunk) streams together hold fewer than 2^31 tiles of 16 tokens.
     const long long max_tiles = (long long)p.batch * p.kv_heads * out.n_chunks * ((p.max_context_length + 15LL) / 16);
-    const uint32_t route_flags = p.flags & (PA_FLAG_FORCE_SPLIT | PA_FLAG_FORCE_SINGLE);
-    out.balanced = p.partition_size == 0 && route_flags == 0 && p.batch <= kMaxBalancedBatch &&
-                   max_tiles <= INT32_MAX;
+    const uint32_t route_flags = p.flags & (PA_FLAG_FORCE_SPLIT | PA_FLAG_FORCE_SINGLE | PA_FLAG_FIXED_PARTITIONS);
+    const bool balanced_capable = route_flags == 0 && p.batch <= kMaxBalancedBatch && max_tiles <= INT32_MAX;
+    out.balanced = balanced_capable && p.partition_size == 0;
+    out.partition_balanced = balanced_capable && p.partition_size > 0;
     out.debug_bounds = (p.flags & PA_FLAG_DEBUG_BOUNDS) != 0;
     out.single_launch = (p.flags & PA_FLAG_SINGLE_LAUNCH) != 0;
     // one launch needs the default route: no partition size, no route flag
@@ -101,6 +105,7 @@ int build_plan(const pa_problem* in, Plan* pl) {
     if (partition % p.page_size) return PA_ERR_INVALID_ARGUMENT;
     if (!out.balanced && partition / p.page_size > kMaxPartitionPages) return PA_ERR_UNSUPPORTED;
     p.partition_size = out.balanced ? 0 : partition;
+    // the fixed route's limits hold whenever it may run (a partition size may still take it)
     out.prob = p;
     out.partition = partition;
     long long nparts = ((long long)p.max_context_length + partition - 1) / partition;
@@ -115,7 +120,7 @@ int build_plan(const pa_problem* in, Plan* pl) {
     if (mgrid > INT32_MAX || (!out.balanced && grid > INT32_MAX)) return PA_ERR_UNSUPPORTED;
     out.decode_grid = grid;
     out.merge_grid = mgrid;
-    if (out.balanced) {
+    if (balanced_capable) {
         const int streams = p.kv_heads * out.n_chunks;
         out.bal_waves = balanced_waves(streams);
         out.spw = gcd(streams, out.bal_waves);
@@ -127,14 +132,33 @@ int build_plan(const pa_problem* in, Plan* pl) {
         if ((long long)p.batch * (streams / out.spw) < kFewBands && out.spw % 2 == 0) out.spw /= 2;
         out.waves_per_stream = out.bal_waves / out.spw;
         out.bands = streams / out.spw;
-        out.need_merge = true;
         out.rows_per_wg = (size_t)2 * out.spw * out.heads_per_wg;
-    } else {
-        out.need_merge = out.force_split || out.n_part_max > 1;
+        // units (band, 16-token tile) of the whole batch at most, from the host's bound
+        out.balanced_units_max = (long long)out.bands * p.batch * ((p.max_context_length + 15LL) / 16);
     }
+    out.need_merge = out.balanced || out.force_split || out.n_part_max > 1;
     out.ws_bytes = workspace_layout(out, kMaxBalancedWG).bytes;
+    if (out.partition_balanced) {
+        const size_t b = workspace_layout(as_balanced(out), kMaxBalancedWG).bytes;
+        if (b > out.ws_bytes) out.ws_bytes = b;
+    }
     *pl = out;
     return PA_OK;
+}
+
+Plan as_balanced(const Plan& pl) {
+    Plan r = pl;
+    r.balanced = true;
+    r.need_merge = true;
+    return r;
+}
+
+bool balanced_partials_fit(const Plan& pl, int cus) {
+    if (!pl.partition_balanced || cus <= 0) return false;
+    // A workgroup's range holds at most ceil(units / grid) units, so no partial covers more
+    // than 16 times that many tokens of a stream.
+    const long long per_wg = (pl.balanced_units_max + cus - 1) / cus;
+    return 16 * per_wg <= pl.prob.partition_size;
 }
 
 WsLayout workspace_layout(const Plan& pl, int wg_slots) {
@@ -222,8 +246,10 @@ pa_status pa_decode(const pa_handle* handle, const void* query, const void* key_
         if (!workspace || workspace_bytes < pl.ws_bytes) return PA_ERR_WORKSPACE;
         if (!aligned16(workspace)) return PA_ERR_MISALIGNED;
     }
-    hipError_t err = pa::launch(pl, query, key_cache, value_cache, block_tables, context_lengths,
-                                scale, out, workspace, pa::workspace_layout(pl, pa::kMaxBalancedWG),
+    // a partition size that the balanced route's partials respect on this device takes it
+    const pa::Plan run = pa::balanced_partials_fit(pl, pa::device_compute_units()) ? pa::as_balanced(pl) : pl;
+    hipError_t err = pa::launch(run, query, key_cache, value_cache, block_tables, context_lengths,
+                                scale, out, workspace, pa::workspace_layout(run, pa::kMaxBalancedWG),
                                 stream);
     return err == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
@@ -235,8 +261,10 @@ pa_status pa_decode_noalloc(const pa_handle* handle, const void* query, const vo
     const pa_status st = check_decode_args(handle, query, key_cache, value_cache, block_tables,
                                            context_lengths, scale, out);
     if (st != PA_OK) return st;
-    const pa::Plan& pl = handle->plan;
-    if (pl.debug_bounds) return PA_ERR_INVALID_ARGUMENT;   // its bitmap needs a caller workspace
+    const pa::Plan& plan = handle->plan;
+    if (plan.debug_bounds) return PA_ERR_INVALID_ARGUMENT;   // its bitmap needs a caller workspace
+    const int cus = plan.partition_balanced ? pa::device_compute_units() : 0;
+    const pa::Plan pl = pa::balanced_partials_fit(plan, cus) ? pa::as_balanced(plan) : plan;
     void* scratch = nullptr;
     pa::WsLayout layout{0, 0, 0, 0, 0, 0, 0};
     if (pl.need_merge) {

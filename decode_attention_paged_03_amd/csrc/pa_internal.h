@@ -39,6 +39,9 @@ struct Plan {
     int heads_per_wg;       // query heads one workgroup serves (divides group, <= 8)
     int n_chunks;           // group / heads_per_wg
     bool balanced;          // route: even split of all token tiles over a resident grid
+    bool partition_balanced;  // a partition size was given and the balanced route may run
+                              // (when its partials fit it: balanced_partials_fit)
+    long long balanced_units_max;  // balanced route: bound on the batch's (band, tile) units
     int bal_waves;          // balanced route: waves per workgroup (8, 12 or 16)
     int spw;                // balanced route: streams a workgroup reads side by side
     int waves_per_stream;   // balanced route: bal_waves / spw
@@ -74,6 +77,12 @@ struct WsLayout {
     int wg_slots;           // balanced route: workgroups the partial rows are sized for
 };
 WsLayout workspace_layout(const Plan& plan, int wg_slots);
+
+// The plan with the balanced route chosen (a partition-size plan whose partials fit).
+Plan as_balanced(const Plan& plan);
+// Whether, on a device with `cus` compute units, every partial of the balanced route covers
+// at most the problem's partition size (then that route honours it and runs).
+bool balanced_partials_fit(const Plan& plan, int cus);
 
 // Host-only validation + planning; returns a pa_status.
 int build_plan(const pa_problem* p, Plan* out);

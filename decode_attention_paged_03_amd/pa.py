@@ -31,6 +31,7 @@ PA_FLAG_FORCE_SPLIT = 0x1
 PA_FLAG_FORCE_SINGLE = 0x2
 PA_FLAG_DEBUG_BOUNDS = 0x4
 PA_FLAG_SINGLE_LAUNCH = 0x8
+PA_FLAG_FIXED_PARTITIONS = 0x10
 
 EXPORTED = ("pa_create", "pa_workspace_size", "pa_decode", "pa_decode_noalloc", "pa_append",
             "pa_destroy", "pa_status_string")

@@ -72,6 +72,10 @@ typedef enum pa_status {
 /* Flags for pa_problem.flags */
 #define PA_FLAG_FORCE_SPLIT  0x1u /* route every sequence through partition triples + merge */
 #define PA_FLAG_FORCE_SINGLE 0x2u /* one partition per sequence (partition = max context)     */
+/* Partitions of exactly partition_size tokens, counted from token 0 (the PARTITION_SIZE
+ * scheme of the "paged_attention_v2_pytorch.py" commit page), even when the default split
+ * would keep every partial within partition_size (see pa_problem.partition_size). */
+#define PA_FLAG_FIXED_PARTITIONS 0x10u
 /* Record block-table entries outside the pool.  Every call treats a table entry that a
  * context dereferences but that lies outside [0, num_physical_pages) as a page of zero
  * keys and values: it is never read, so it cannot fault.  (The first page's "Baseline"
@@ -106,8 +110,14 @@ typedef struct pa_problem {
     int32_t max_pages_per_sequence; /* row stride of block_tables                                 */
     int32_t num_physical_pages;     /* pages in each of key_cache / value_cache (pa_append writes
                                        only below it)                                             */
-    int32_t partition_size;         /* tokens per partition, multiple of page_size, at most
-                                       512 pages; 0 -> the library's default                      */
+    int32_t partition_size;         /* 0: the library splits the work (default).  > 0: no
+                                       partial (max, sum, acc) triple covers more than this many
+                                       tokens of a context; a multiple of page_size, at most 512
+                                       pages.  The default split runs when the problem's sizes
+                                       guarantee that on the device (every workgroup's share is
+                                       at most partition_size tokens per stream); otherwise, or
+                                       with PA_FLAG_FIXED_PARTITIONS or a FORCE flag, fixed
+                                       partitions of exactly this many tokens                     */
     int32_t max_context_length;     /* bound on every context_lengths[b]; sizes the grid and the
                                        workspace; 0 -> max_pages_per_sequence * page_size          */
     uint32_t flags;                 /* PA_FLAG_*                                                  */

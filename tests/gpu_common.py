@@ -78,8 +78,23 @@ def check_against_oracle(got: np.ndarray, ref: np.ndarray, what: str = ""):
     return worst
 
 
+FIXED = pa.PA_FLAG_FIXED_PARTITIONS
+
+
+def fixed_flags(partition_size) -> int:
+    """The flag that keeps a partition size on the fixed-partition route (0 for none)."""
+    return FIXED if partition_size else 0
+
+
 def decode_and_check(wl, *, partition_size=None, flags=0, rows=None, guard=True, what=None):
+    """pa_decode against the oracle.  A partition size given here means the fixed-partition
+    route (PA_FLAG_FIXED_PARTITIONS); tests of the library's own choice pass the flag
+    themselves through ``pa.decoder_for``."""
     what = what or wl.name
+    if partition_size is None:
+        partition_size = wl.partition_size
+    if partition_size and not flags:
+        flags = FIXED
     say(f"[case] {what}: {wl.summary()} partition={partition_size} flags={flags}")
     dev = Device(wl, guard=guard)
     dec = pa.decoder_for(wl, partition_size=partition_size, flags=flags)

@@ -76,7 +76,9 @@ def create_status(prob):
     (dict(partition_size=16 * 513), pa.PA_ERR_UNSUPPORTED),
     (dict(max_context_length=8 * 16 + 1), pa.PA_ERR_INVALID_ARGUMENT),
     (dict(flags=0x100), pa.PA_ERR_INVALID_ARGUMENT),
-    (dict(flags=0x10), pa.PA_ERR_INVALID_ARGUMENT),
+    (dict(flags=0x20), pa.PA_ERR_INVALID_ARGUMENT),
+    (dict(flags=pa.PA_FLAG_FIXED_PARTITIONS, partition_size=16), pa.PA_OK),
+    (dict(flags=pa.PA_FLAG_FIXED_PARTITIONS | pa.PA_FLAG_SINGLE_LAUNCH), pa.PA_ERR_INVALID_ARGUMENT),
     (dict(flags=pa.PA_FLAG_DEBUG_BOUNDS), pa.PA_OK),
     (dict(flags=pa.PA_FLAG_DEBUG_BOUNDS | pa.PA_FLAG_FORCE_SPLIT), pa.PA_OK),
     (dict(flags=pa.PA_FLAG_SINGLE_LAUNCH), pa.PA_OK),
@@ -123,12 +125,19 @@ def test_workspace_size():
     # batch 16 of 4 KV heads: 16 bands of 4 streams -> 2 side by side (32 bands would not be
     # halved again); batch 32: 32 bands of 4, kept
     assert ws_size(query_heads=24, kv_heads=4, batch=32) == 1024 * 2 * 4 * 6 * (128 + 2) * 4 + 1024 * 32
-    # fixed partitions of one page -> 8 partitions of (D + 2) floats per (sequence, head)
-    assert ws_size(partition_size=16) == 2 * 8 * 8 * (128 + 2) * 4
-    assert ws_size(partition_size=16, max_context_length=40) == 2 * 8 * 3 * (128 + 2) * 4
-    # 128 tokens fit one fixed partition of 1024: no workspace unless split is forced
-    assert ws_size(partition_size=1024) == 0
+    # a partition size may run either route (the balanced one when its partials fit it):
+    # the larger of the two layouts.  Fixed partitions of one page -> 8 partitions of
+    # (D + 2) floats per (sequence, head); the balanced layout as without a size.
+    bal = ws_size()
+    assert ws_size(partition_size=16) == max(2 * 8 * 8 * (128 + 2) * 4, bal)
+    assert ws_size(partition_size=16, max_context_length=40) == max(2 * 8 * 3 * (128 + 2) * 4, bal)
+    assert ws_size(partition_size=1024) == bal
+    # the route flags take fixed partitions only: 128 tokens fit one partition of 1024, no
+    # workspace unless split is forced
     assert ws_size(flags=pa.PA_FLAG_FORCE_SPLIT) == 2 * 8 * 1 * (128 + 2) * 4
+    # PA_FLAG_FIXED_PARTITIONS keeps a partition size on the fixed route: its layout only
+    assert ws_size(partition_size=16, flags=pa.PA_FLAG_FIXED_PARTITIONS) == 2 * 8 * 8 * (128 + 2) * 4
+    assert ws_size(partition_size=1024, flags=pa.PA_FLAG_FIXED_PARTITIONS) == 0
     assert ws_size(flags=pa.PA_FLAG_FORCE_SINGLE, max_pages_per_sequence=64) == 0
 
 
@@ -144,7 +153,7 @@ def test_workspace_size_with_bounds_bitmap():
     # bytes; it keeps the balanced route and needs a workspace even without a merge
     D = pa.PA_FLAG_DEBUG_BOUNDS
     assert ws_size(flags=D) == 256 + ws_size()
-    assert ws_size(flags=D, partition_size=1024) == 256
+    assert ws_size(flags=D | pa.PA_FLAG_FORCE_SINGLE) == 256
     assert ws_size(flags=D, batch=100, max_pages_per_sequence=100,
                    num_physical_pages=20000) == 1280 + ws_size(batch=100, max_pages_per_sequence=100,
                                                                num_physical_pages=20000)

@@ -56,7 +56,7 @@ def test_out_of_pool_entries(shape, route, debug):
     flags = pa.PA_FLAG_DEBUG_BOUNDS if debug else 0
     C.say(f"[case] out-of-pool entries {shape[:4]} route {route} debug {debug}: {len(inside)} planted")
     dev = C.Device(wl, guard=True, guard_after=GUARD_AFTER)
-    dec = pa.decoder_for(wl, partition_size=part, flags=flags)
+    dec = pa.decoder_for(wl, partition_size=part, flags=flags | C.fixed_flags(part))
     try:
         if dec.workspace is not None:
             dec.workspace.fill_(0xFF)        # every bitmap word must be written by the call

@@ -46,7 +46,7 @@ def test_workspace_garbage_ignored(partition):
     wl = W.make_named("small_batch")
     C.say(f"[case] garbage workspace, partition {partition}")
     dev = C.Device(wl)
-    dec = pa.decoder_for(wl, partition_size=partition)
+    dec = pa.decoder_for(wl, partition_size=partition, flags=C.fixed_flags(partition))
     try:
         assert dec.workspace is not None
         dec.workspace.fill_(0xFF)
@@ -118,7 +118,8 @@ def test_max_context_length_bound(partition):
                          max_pages_per_sequence=200, pool="holes10", seed=7600)
     C.say(f"[case] max_context_length 1000 (table allows {200 * 16}), partition {partition}")
     dev = C.Device(wl)
-    dec = pa.decoder_for(wl, partition_size=partition, max_context_length=1000)
+    dec = pa.decoder_for(wl, partition_size=partition, max_context_length=1000,
+                         flags=C.fixed_flags(partition))
     try:
         out = dev.run(dec).cpu().numpy()
     finally:

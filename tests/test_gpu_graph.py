@@ -55,7 +55,7 @@ def test_decode_graph_replays(partition):
     import torch
     wl = W.make_named("small_batch")
     dev = C.Device(wl)
-    dec = pa.decoder_for(wl, partition_size=partition)
+    dec = pa.decoder_for(wl, partition_size=partition, flags=C.fixed_flags(partition))
     rng = np.random.default_rng(9100 + partition)
     out = torch.full((wl.batch, wl.query_heads, wl.head_dim), float("nan"), device="cuda")
     try:

@@ -51,7 +51,8 @@ CTX = list(range(2, 17)) + [64, 300, 2000]
 def test_wide_values(family, shape, route):
     label, vd, vf, kf = family
     QH, KVH, D, ps = shape
-    kw = dict(balanced=dict(partition_size=0), partition_1page=dict(partition_size=ps),
+    kw = dict(balanced=dict(partition_size=0),
+              partition_1page=dict(partition_size=ps, flags=pa.PA_FLAG_FIXED_PARTITIONS),
               single=dict(flags=pa.PA_FLAG_FORCE_SINGLE))[route]
     wl = W.make_workload(name="wide", batch=len(CTX), query_heads=QH, kv_heads=KVH, head_dim=D,
                          page_size=ps, context_lengths=CTX, pool="holes10",

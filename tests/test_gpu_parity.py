@@ -45,7 +45,7 @@ def test_mixed128_full():
     dev = C.Device(wl)
     outs = {}
     for part in (0, 1024):
-        dec = pa.decoder_for(wl, partition_size=part)
+        dec = pa.decoder_for(wl, partition_size=part, flags=C.fixed_flags(part))
         try:
             outs[part] = dev.run(dec).cpu().numpy()
         finally:
@@ -53,6 +53,43 @@ def test_mixed128_full():
     ref = C.oracle.attend_workload(wl, nthreads=C.oracle_threads())
     for part, out in outs.items():
         C.check_against_oracle(out, ref, f"mixed128 all rows, partition {part}")
+
+
+# ------------------------------------------- a partition size: the library's route choice
+
+def _bits(wl, part, flags=0):
+    import torch
+    dec = pa.decoder_for(wl, partition_size=part, flags=flags)
+    try:
+        return C.Device(wl).run(dec).clone().view(torch.int32)
+    finally:
+        dec.close()
+
+
+@pytest.mark.parametrize("name", ["batch64", "long100k", "small_batch"])
+def test_partition_size_within_balanced_partials(name):
+    """partition_size 1024 without PA_FLAG_FIXED_PARTITIONS: on a part with 256 or more
+    compute units the balanced split's partials are at most 1024 tokens (batch64: 64 units
+    per workgroup at most; long100k: 49; small_batch: 32), so the library runs that route --
+    bit for bit the default's output."""
+    import torch
+    if torch.cuda.get_device_properties(0).multi_processor_count < 256:
+        pytest.skip("the bound is computed for 256 compute units")
+    wl = W.make_named(name)
+    C.say(f"[case] partition 1024 takes the balanced route: {name}")
+    assert torch.equal(_bits(wl, 1024), _bits(wl, 0))
+
+
+def test_partition_size_beyond_balanced_partials():
+    """mixed128 with partition_size 1024: the host's bound on a balanced partial (32,768
+    tokens per stream, from 1024 table pages of 32) passes 1024, so the fixed partitions run --
+    bit for bit PA_FLAG_FIXED_PARTITIONS's output, and not the default's."""
+    import torch
+    wl = W.make_named("mixed128")
+    C.say("[case] partition 1024 on mixed128 keeps fixed partitions")
+    fixed = _bits(wl, 1024, pa.PA_FLAG_FIXED_PARTITIONS)
+    assert torch.equal(_bits(wl, 1024), fixed)
+    assert not torch.equal(_bits(wl, 0), fixed)
 
 
 # ------------------------------------------------------- forced single / split routes
@@ -116,7 +153,7 @@ def test_repeat_bitwise_and_streams(partition):
     import torch
     wl = W.make_named("small_batch")
     dev = C.Device(wl)
-    dec = pa.decoder_for(wl, partition_size=partition)
+    dec = pa.decoder_for(wl, partition_size=partition, flags=C.fixed_flags(partition))
     try:
         a = dev.run(dec).clone()
         for _ in range(5):
@@ -143,7 +180,7 @@ def test_page_relabel_bitwise(partition):
     wl2 = W.Workload(**{**wl.__dict__, "key_cache": k, "value_cache": v, "block_tables": bt})
     outs = []
     for w in (wl, wl2):
-        dec = pa.decoder_for(w, partition_size=partition)
+        dec = pa.decoder_for(w, partition_size=partition, flags=C.fixed_flags(partition))
         try:
             outs.append(C.Device(w).run(dec).clone())
         finally:

@@ -43,7 +43,7 @@ def test_noalloc_two_calls_match_pa_decode(route):
         for wl in cases:
             C.say(f"[case] noalloc {route}: {wl.summary()}")
             dev = C.Device(wl)
-            dec = pa.decoder_for(wl, partition_size=part)
+            dec = pa.decoder_for(wl, partition_size=part, flags=C.fixed_flags(part))
             devs.append(dev)
             decs.append(dec)
             refs.append(dev.run(dec).clone())           # pa_decode, caller workspace
