@@ -720,10 +720,62 @@ pa_merge_kernel(MergeArgs a) {
     const int bh = blockIdx.x;
     const int b = bh / a.query_heads;
     const int ctx = a.ctx[b];
-    const int n = (ctx + a.partition - 1) / a.partition;
-    if (n == 0 || (n == 1 && !a.force_split)) return;   // written by the decode kernel
+    const int n = min((ctx + a.partition - 1) / a.partition, a.n_part_max);
+    if (n <= 0 || (n == 1 && !a.force_split)) return;   // written by the decode kernel
     const size_t r0 = (size_t)bh * a.n_part_max;
     combine_rows<D>(a.ws_ml, a.ws_acc, r0, r0 + 1, 1, n, a.out + (size_t)bh * D);
+}
+
+// Fixed-partition route, rows with few partitions: one thread per (output row, float4
+// column), kMergeThreads / (D / 4) rows per block.  A thread folds its column over the
+// row's partitions in batches of kRowFoldUnroll (every load of a batch issued before any
+// is used), so a row with n partitions costs ceil(n / kRowFoldUnroll) round trips and a
+// row written by the decode kernel (one partition) nothing.  Used when no row can have
+// more than kRowFoldMax partitions; longer rows take pa_merge_kernel.
+constexpr int kRowFoldUnroll = 8;
+constexpr int kRowFoldMax = 32;
+
+template <int D>
+__global__ void __launch_bounds__(kMergeThreads)
+pa_merge_rows_kernel(MergeArgs a, int rows) {
+    constexpr int C4 = D / 4;
+    constexpr int RPB = kMergeThreads / C4;
+    const int row = blockIdx.x * RPB + (int)threadIdx.x / C4;   // b * query_heads + h
+    const int c4 = (int)threadIdx.x % C4;
+    if (row >= rows) return;
+    // (a length past the plan's bound is a broken precondition: its row reads no slot past
+    // its own)
+    const int n = min((a.ctx[row / a.query_heads] + a.partition - 1) / a.partition, a.n_part_max);
+    if (n <= 0 || (n == 1 && !a.force_split)) return;   // written by the decode kernel
+    const size_t base = (size_t)row * a.n_part_max;
+    float m = -INFINITY, l = 0.f;
+    float4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int p0 = 0; p0 < n; p0 += kRowFoldUnroll) {
+        float4_t pa[kRowFoldUnroll];
+        float pm[kRowFoldUnroll], pl[kRowFoldUnroll];
+#pragma unroll
+        for (int k = 0; k < kRowFoldUnroll; ++k) {
+            const size_t slot = base + (p0 + k < n ? p0 + k : p0);   // past the row: weight 0
+            pa[k] = reinterpret_cast<const float4_t*>(a.ws_acc + slot * D)[c4];
+            pm[k] = p0 + k < n ? a.ws_ml[slot * 2] : -INFINITY;
+            pl[k] = a.ws_ml[slot * 2 + 1];
+        }
+        float M = m;
+#pragma unroll
+        for (int k = 0; k < kRowFoldUnroll; ++k) M = fmaxf(M, pm[k]);
+        // partition 0 holds token 0, so M is finite from the first batch on
+        const float a0 = fast_exp2(m - M);      // 0 while nothing was folded in yet
+        l *= a0;
+        acc *= a0;
+#pragma unroll
+        for (int k = 0; k < kRowFoldUnroll; ++k) {
+            const float e = fast_exp2(pm[k] - M);
+            l += e * pl[k];
+            acc += e * pa[k];
+        }
+        m = M;
+    }
+    reinterpret_cast<float4_t*>(a.out + (size_t)row * D)[c4] = acc / l;
 }
 
 // ------------------------------------------------------------------------------------
@@ -1766,7 +1818,10 @@ pa_bad_entries_kernel(const int32_t* bt, const int32_t* ctx, int max_pages, int 
 #define PA_WAVES 4   // waves per decode workgroup (fixed route)
 #endif
 #ifndef PA_DEPTH
-#define PA_DEPTH 2   // tile buffers per wave (fixed route)
+// tile buffers per wave (fixed route): one buffer leaves registers for more resident waves;
+// measured against two (4 waves per workgroup, partitions of 1024): batch64 77.0 vs
+// 83.5 us, long100k 49.9 vs 51.1, mixed128 281.6 vs 300.6; 8 or 12 waves were no faster
+#define PA_DEPTH 1
 #endif
 #ifndef PA_BAL_DEPTH
 #define PA_BAL_DEPTH 1   // tile buffers per wave (balanced route)
@@ -1941,12 +1996,21 @@ hipError_t launch(const Plan& pl, const void* q, const void* k, const void* v,
     ma.partition = pl.partition;
     ma.n_part_max = pl.n_part_max;
     ma.force_split = da.force_split;
-    if (p.head_dim == 128)
+    if (pl.n_part_max <= kRowFoldMax) {
+        const int rows = (int)pl.merge_grid;   // batch * query_heads
+        const int rpb = kMergeThreads / (p.head_dim / 4);
+        const dim3 grid((unsigned)((rows + rpb - 1) / rpb));
+        if (p.head_dim == 128)
+            hipLaunchKernelGGL(pa_merge_rows_kernel<128>, grid, dim3(kMergeThreads), 0, stream, ma, rows);
+        else
+            hipLaunchKernelGGL(pa_merge_rows_kernel<64>, grid, dim3(kMergeThreads), 0, stream, ma, rows);
+    } else if (p.head_dim == 128) {
         hipLaunchKernelGGL(pa_merge_kernel<128>, dim3((unsigned)pl.merge_grid), dim3(kMergeThreads), 0,
                            stream, ma);
-    else
+    } else {
         hipLaunchKernelGGL(pa_merge_kernel<64>, dim3((unsigned)pl.merge_grid), dim3(kMergeThreads), 0,
                            stream, ma);
+    }
     return hipGetLastError();
 }
 
