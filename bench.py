@@ -160,9 +160,9 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str) -> str:
     lines = [f"# HBM traffic of one pa_decode call, workload {workload}",
              f"kernel_source_sha256: {kernel_source_hash()}",
              f"command_fetch: rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o run -- python bench.py --workload {workload} "
-             "--steps 10 --warmup 2 --no-cpu-baseline --copy-calibration --append-steps 0",
+             "--also none --steps 10 --warmup 2 --no-cpu-baseline --copy-calibration --append-steps 0",
              f"command_write: rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o run -- python bench.py --workload {workload} "
-             "--steps 10 --warmup 2 --no-cpu-baseline --copy-calibration --append-steps 0",
+             "--also none --steps 10 --warmup 2 --no-cpu-baseline --copy-calibration --append-steps 0",
              f"calibration: plain device copy of {COPY_BYTES} B; bytes = counter KiB * 1024 * factor",
              f"fetch_factor: {out['FETCH_SIZE'][0]:.4f}",
              f"write_factor: {out['WRITE_SIZE'][0]:.4f}"]
@@ -220,8 +220,8 @@ def summarize_counters(folders, workload: str) -> str:
              f"kernel_source_sha256: {kernel_source_hash()}"]
     for p in COUNTER_PASSES:
         lines.append(f"command: rocprofv3 --pmc {' '.join(p)} --output-format csv -d <dir> -o run -- "
-                     f"python bench.py --workload {workload} --steps 10 --warmup 2 --no-cpu-baseline "
-                     "--append-steps 0")
+                     f"python bench.py --workload {workload} --also none --steps 10 --warmup 2 "
+                     "--no-cpu-baseline --append-steps 0")
     lines.append("(mean per dispatch, warm-up dispatches included)")
     for k, cs in per.items():
         lines.append(f"{k}:")
@@ -274,7 +274,7 @@ def summarize_trace(folder: str, workload: str, steps: int = 200) -> str:
     lines = [f"# rocprofv3 kernel statistics, workload {workload}",
              f"kernel_source_sha256: {kernel_source_hash()}",
              f"command: rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o run -- python bench.py "
-             f"--workload {workload} --steps {steps} --no-cpu-baseline",
+             f"--workload {workload} --also none --steps {steps} --no-cpu-baseline",
              "(calls include the warm-up calls; durations in microseconds)",
              f"{'kernel':<48} {'calls':>6} {'avg_us':>9} {'min_us':>9} {'max_us':>9}"]
     per_call = 0.0
