@@ -135,8 +135,16 @@ int build_plan(const pa_problem* in, Plan* pl) {
         out.rows_per_wg = (size_t)2 * out.spw * out.heads_per_wg;
         // units (band, 16-token tile) of the whole batch at most, from the host's bound
         out.balanced_units_max = (long long)out.bands * p.batch * ((p.max_context_length + 15LL) / 16);
+        // Short bands only (the host's bound): one workgroup per band finishes every stream
+        // in LDS, so neither a merge launch nor a workspace is needed.  The spread of the
+        // even split over all compute units would leave most of them idle anyway and split
+        // each band over many workgroups.
+        const long long band_tiles = (p.max_context_length + 15LL) / 16 * out.spw;
+        out.band_per_wg = out.balanced && band_tiles <= kBandPerWgMaxTiles &&
+                          (long long)p.batch * out.bands <= kMaxBalancedWG;
+        if (out.band_per_wg) out.single_launch = false;   // one kernel already
     }
-    out.need_merge = out.balanced || out.force_split || out.n_part_max > 1;
+    out.need_merge = (out.balanced && !out.band_per_wg) || out.force_split || out.n_part_max > 1;
     out.ws_bytes = workspace_layout(out, kMaxBalancedWG).bytes;
     if (out.partition_balanced) {
         const size_t b = workspace_layout(as_balanced(out), kMaxBalancedWG).bytes;
@@ -149,6 +157,7 @@ int build_plan(const pa_problem* in, Plan* pl) {
 Plan as_balanced(const Plan& pl) {
     Plan r = pl;
     r.balanced = true;
+    r.band_per_wg = false;
     r.need_merge = true;
     return r;
 }

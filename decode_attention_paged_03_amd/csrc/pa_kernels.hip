@@ -1097,7 +1097,8 @@ __device__ __forceinline__ void single_launch_merge(const DecodeArgs& a, int w, 
     }
 }
 
-template <int D, int HP, int DEPTH, int NW, bool SPLIT, bool KROW>
+// BANDWG: one workgroup per (sequence, band) -- the plan's choice for short bands.
+template <int D, int HP, int DEPTH, int NW, bool SPLIT, bool KROW, bool BANDWG>
 __global__ void __launch_bounds__(NW * 64)
 pa_decode_balanced(DecodeArgs a) {
     using G = Geo<D>;
@@ -1153,9 +1154,14 @@ pa_decode_balanced(DecodeArgs a) {
 
     const int N = SG * plane;
     const int NWG = gridDim.x;
-    const int w = PA_XCD_REMAP ? xcd_major((int)blockIdx.x, NWG) : (int)blockIdx.x;
-    const int g0 = split_point(w, N, NWG);
-    const int g1 = split_point(w + 1, N, NWG);
+    // One workgroup per (sequence, band) when every band is short (the plan's choice): the
+    // workgroup's units are exactly its band's, so every stream is finished here.
+    constexpr bool bandwg = BANDWG;
+    const int w = bandwg ? (int)blockIdx.x : PA_XCD_REMAP ? xcd_major((int)blockIdx.x, NWG) : (int)blockIdx.x;
+    const int wb = w / SG;                    // band mode: the sequence and band of this workgroup
+    const int wband = w - wb * SG;
+    const int g0 = bandwg ? SG * s_pref[wb] + wband * (s_pref[wb + 1] - s_pref[wb]) : split_point(w, N, NWG);
+    const int g1 = bandwg ? g0 + (s_pref[wb + 1] - s_pref[wb]) : split_point(w + 1, N, NWG);
     auto run_start = [&](int r) {   // cumulative weight of runs 0 .. r-1, over the total
         if (RW == 1) return r == 0 ? g0 : g1;
         const long long cum = (long long)r * (RW - 1) * (100 + PA_RUN_SKEW) - (long long)PA_RUN_SKEW * r * (r - 1);
@@ -1398,7 +1404,7 @@ pa_decode_balanced(DecodeArgs a) {
                 __builtin_amdgcn_sched_barrier(0);
                 if (i + d == 0) {
                     clear_my_slots();
-                    if (wave == NW - 1) write_records();
+                    if (wave == NW - 1 && !bandwg) write_records();
                 }
                 if constexpr (DEPTH == 1) consume(dsc[d], kb[d], vb[d], qb, i + d);
                 else if (i + d < nk) consume(dsc[d], kb[d], vb[d], qr[d], i + d);
@@ -1440,9 +1446,9 @@ pa_decode_balanced(DecodeArgs a) {
     }
     if (nk == 0) {
         clear_my_slots();
-        if (wave == NW - 1) write_records();
+        if (wave == NW - 1 && !bandwg) write_records();
     }
-    if (g1 == g0) {
+    if (g1 == g0 && !bandwg) {
         // no units: empty triples (weight 0) for a merge whose band spans this
         // workgroup's (empty) range
         const size_t wslot = (size_t)w * 2 * SPW * HP;
@@ -1529,7 +1535,7 @@ pa_decode_balanced(DecodeArgs a) {
             const size_t row0 = (size_t)b * a.query_heads + kvh * a.group + chunk * HP;
             if (tb == U0 && te == U0 + Tb) {
                 reinterpret_cast<float4_t*>(a.out + (row0 + h) * D)[d4] = o / Ls;
-            } else {
+            } else if (!bandwg) {   // (a band held by one workgroup is always complete)
                 const size_t wrow = (((size_t)w * 2 + (tb == g0 ? 0 : 1)) * SPW + spr) * HP + h;
                 reinterpret_cast<float4_t*>(a.ws_acc + wrow * D)[d4] = o;
                 if (d4 == 0) {
@@ -1851,17 +1857,21 @@ hipError_t launch_balanced_nw(const Plan& pl, const DecodeArgs& args, int ws_slo
     // kernel's LDS still fits next to the per-sequence arrays; otherwise K is loaded in
     // the MFMA layout.
     // (the staging is per wave: with 16 waves it would not fit next to the partial slots)
-    const auto kern_row = pa_decode_balanced<D, HP, kBalDepth, NW, SPLIT, PA_KROW && D == 128 && NW <= 12>;
-    const auto kern_mfma = pa_decode_balanced<D, HP, kBalDepth, NW, SPLIT, false>;
+    constexpr bool kRow = PA_KROW && D == 128 && NW <= 12;
     const size_t lds = (size_t)(2 * pl.prob.batch + 1) * sizeof(int);
-    static const size_t row_static = static_lds_bytes(kern_row);
-    const auto kern = (row_static != SIZE_MAX && row_static + lds <= kLdsPerWorkgroup) ? kern_row : kern_mfma;
-    const int grid = balanced_grid();
+    static const size_t row_static = static_lds_bytes(pa_decode_balanced<D, HP, kBalDepth, NW, SPLIT, kRow, false>);
+    const bool use_row = row_static != SIZE_MAX && row_static + lds <= kLdsPerWorkgroup;
+    const auto kern = pl.band_per_wg
+                          ? (use_row ? pa_decode_balanced<D, HP, kBalDepth, NW, SPLIT, kRow, true>
+                                     : pa_decode_balanced<D, HP, kBalDepth, NW, SPLIT, false, true>)
+                          : (use_row ? pa_decode_balanced<D, HP, kBalDepth, NW, SPLIT, kRow, false>
+                                     : pa_decode_balanced<D, HP, kBalDepth, NW, SPLIT, false, false>);
+    const int grid = pl.band_per_wg ? pl.prob.batch * pl.bands : balanced_grid();
     if (grid <= 0) return hipErrorInvalidDevice;
-    if (grid > ws_slots) return hipErrorInvalidValue;   // the workspace holds fewer workgroups' rows
+    if (!pl.band_per_wg && grid > ws_slots) return hipErrorInvalidValue;   // the workspace holds fewer workgroups' rows
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NW * 64), lds, stream, args);
     hipError_t err = hipGetLastError();
-    if (err != hipSuccess || args.single_launch) return err;
+    if (err != hipSuccess || args.single_launch || pl.band_per_wg) return err;
     hipLaunchKernelGGL((pa_merge_balanced<D, HP>), dim3((unsigned)grid), dim3(kMergeThreads), 0, stream, args);
     return hipGetLastError();
 }

@@ -137,6 +137,30 @@ def test_shapes(shape, partition):
     C.decode_and_check(wl, what=f"shape {shape} partition {part}")
 
 
+SHORT = [
+    # (QH, KVH, D, ps, ctx): every band within the one-workgroup-per-band limit (at most 24
+    # stream tiles), so the call is one kernel and needs no workspace
+    (8, 2, 64, 16, [37, 100]),                  # the tiny workload's shape
+    (32, 8, 128, 16, [1, 95, 60, 0, 17]),       # 2 streams side by side, an empty sequence
+    (24, 4, 128, 8, [3, 64, 100]),              # pages of 8: tiles over two pages
+    (64, 8, 128, 32, [31, 1, 96]),              # 8 heads per wave
+    (16, 16, 64, 16, [40, 0, 2, 16, 17]),       # MHA
+]
+
+
+@pytest.mark.parametrize("shape", SHORT, ids=lambda s: f"qh{s[0]}_kvh{s[1]}_d{s[2]}_ps{s[3]}")
+def test_short_bands_one_workgroup_each(shape):
+    QH, KVH, D, ps, ctx = shape
+    wl = W.make_workload(name="short", batch=len(ctx), query_heads=QH, kv_heads=KVH, head_dim=D,
+                         page_size=ps, context_lengths=ctx, pool="holes10", seed=7200 + QH + D + ps)
+    dec = pa.decoder_for(wl, partition_size=0)
+    try:
+        assert dec.workspace_bytes == 0, "expected the one-workgroup-per-band shortcut"
+    finally:
+        dec.close()
+    C.decode_and_check(wl, partition_size=0, what=f"short bands {shape}")
+
+
 @pytest.mark.parametrize("partition", [0, 256])
 def test_outlier_keys_small(partition):
     """Keys scaled x8 at 1% of positions: many moves of the reference max."""
