@@ -486,15 +486,18 @@ def kernel_resources(kernel_names):
     return out or None
 
 
-def decode_kernel_names(dec, wl):
+def decode_kernel_names(wl, band_per_wg: bool):
     """Names (as in profiles/resources.txt) of the kernels one pa_decode call runs on the
     default (balanced) route: heads per wave = the largest divisor of the group up to 8;
-    pages of 8 split a tile; whole-row K loads at head_dim 128 (when the LDS fits)."""
+    pages of 8 split a tile; whole-row K loads at head_dim 128 (when the LDS fits); with
+    short bands (one workgroup per band, no workspace) no merge kernel."""
     hp = max(h for h in range(1, 9) if wl.group % h == 0)
     split = 1 if wl.page_size < 16 else 0
     krow = 1 if wl.head_dim == 128 else 0
-    return [f"pa_decode_balanced<{wl.head_dim},{hp},1,12,{split},{krow}>",
-            f"pa_merge_balanced<{wl.head_dim},{hp}>"]
+    names = [f"pa_decode_balanced<{wl.head_dim},{hp},1,12,{split},{krow},{int(band_per_wg)}>"]
+    if not band_per_wg:
+        names.append(f"pa_merge_balanced<{wl.head_dim},{hp}>")
+    return names
 
 
 def measure(W, pa, wl, args, stream, steps, warmup, append_steps=0, copy_calibration=False):
@@ -564,7 +567,9 @@ def measure(W, pa, wl, args, stream, steps, warmup, append_steps=0, copy_calibra
         torch.cuda.synchronize()
 
     balanced = dec.problem.partition_size == 0
-    if balanced:
+    if balanced and dec.workspace_bytes == 0:
+        kernel_name = "pa_decode call: pa_decode_balanced, one workgroup per band (no merge)"
+    elif balanced:
         kernel_name = "pa_decode call: pa_decode_balanced + pa_merge_balanced"
     elif fixed:
         kernel_name = "pa_decode call: pa_decode_kernel (+ pa_merge_kernel when split)"
@@ -607,7 +612,8 @@ def measure(W, pa, wl, args, stream, steps, warmup, append_steps=0, copy_calibra
         },
     }
     if balanced:
-        res["roofline"]["resources"] = kernel_resources(decode_kernel_names(dec, wl))
+        # the default route needs no workspace only with one workgroup per band
+        res["roofline"]["resources"] = kernel_resources(decode_kernel_names(wl, dec.workspace_bytes == 0))
     if append_line:
         res["append"] = append_line
     dec.close()

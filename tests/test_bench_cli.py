@@ -98,8 +98,10 @@ def test_committed_resources_cover_the_benched_kernels():
             group = spec["query_heads"] // spec["kv_heads"]
             page_size = spec["page_size"]
             head_dim = spec["head_dim"]
-        names = bench.decode_kernel_names(None, _Wl)
-        assert bench.kernel_resources(names) is not None and len(bench.kernel_resources(names)) == 2, name
+        for band in (False, True):   # the even split, and one workgroup per band
+            names = bench.decode_kernel_names(_Wl, band)
+            got = bench.kernel_resources(names)
+            assert got is not None and len(got) == len(names), (name, band)
 
 
 def test_cpu_baseline_fields():
