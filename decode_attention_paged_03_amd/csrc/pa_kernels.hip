@@ -720,7 +720,7 @@ pa_merge_kernel(MergeArgs a) {
     const int bh = blockIdx.x;
     const int b = bh / a.query_heads;
     const int ctx = a.ctx[b];
-    const int n = min((ctx + a.partition - 1) / a.partition, a.n_part_max);
+    const int n = (int)min(((long long)ctx + a.partition - 1) / a.partition, (long long)a.n_part_max);
     if (n <= 0 || (n == 1 && !a.force_split)) return;   // written by the decode kernel
     const size_t r0 = (size_t)bh * a.n_part_max;
     combine_rows<D>(a.ws_ml, a.ws_acc, r0, r0 + 1, 1, n, a.out + (size_t)bh * D);
@@ -745,7 +745,8 @@ pa_merge_rows_kernel(MergeArgs a, int rows) {
     if (row >= rows) return;
     // (a length past the plan's bound is a broken precondition: its row reads no slot past
     // its own)
-    const int n = min((a.ctx[row / a.query_heads] + a.partition - 1) / a.partition, a.n_part_max);
+    const int n = (int)min(((long long)a.ctx[row / a.query_heads] + a.partition - 1) / a.partition,
+                           (long long)a.n_part_max);
     if (n <= 0 || (n == 1 && !a.force_split)) return;   // written by the decode kernel
     const size_t base = (size_t)row * a.n_part_max;
     float m = -INFINITY, l = 0.f;
@@ -1945,6 +1946,11 @@ hipError_t launch(const Plan& pl, const void* q, const void* k, const void* v,
                   const int32_t* block_tables, const int32_t* ctx, float scale, float* out,
                   void* workspace, const WsLayout& layout, hipStream_t stream) {
     const pa_problem& p = pl.prob;
+    // the single-launch merge folds at most kArrivalGroup groups of kArrivalGroup pieces, so
+    // a band may span at most that many workgroups (checked before anything is enqueued)
+    if (pl.single_launch && pl.balanced && !pl.band_per_wg &&
+        device_compute_units() > kArrivalGroup * kArrivalGroup)
+        return hipErrorInvalidConfiguration;
     float* ws_acc = nullptr;
     float* ws_ml = nullptr;
     int4* ws_desc = nullptr;

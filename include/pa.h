@@ -96,7 +96,9 @@ typedef enum pa_status {
  * above.  The workspace then ends with arrival counters that must be zero before the
  * first call: zero the whole workspace once after allocating it (e.g. hipMemset), and
  * again after using it for any other problem or route.  Every call leaves its counters
- * at zero.  (pa_decode_noalloc keeps its own counters, zero from the start.)  Measured
+ * at zero.  (pa_decode_noalloc keeps its own counters, zero from the start.)  A crossing
+ * band is merged in groups of 16 pieces, 16 groups at most: on a GPU with more than 256
+ * compute units the call fails with PA_ERR_HIP before enqueuing anything.  Measured
  * slower than the two launches on the serving-shaped and long-context workloads: the
  * device-scope arrivals cost more than the second launch. */
 #define PA_FLAG_SINGLE_LAUNCH 0x8u
