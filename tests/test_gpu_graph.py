@@ -143,3 +143,57 @@ def test_append_then_decode_graph_replays():
                 C.check_against_oracle(got_out.cpu().numpy(), exp, "append+decode graph replay")
     finally:
         dec.close()
+
+
+@pytest.mark.parametrize("entry", ["pa_decode", "pa_decode_noalloc"])
+def test_single_launch_graph_replays(entry):
+    """PA_FLAG_SINGLE_LAUNCH (one kernel per call, the merge done by the last arrival)
+    captured once and replayed with new queries and lengths: the arrival counters return
+    to zero within each call, so every replay equals an eager single-launch call bit for
+    bit and leaves the counters at zero.  The no-allocation entry point is captured the
+    same way (its scratch address is looked up in the warm-up call, before capture)."""
+    import torch
+    wl = W.make_named("batch64")
+    dev = C.Device(wl)
+    dec = pa.decoder_for(wl, partition_size=0, flags=pa.PA_FLAG_SINGLE_LAUNCH)
+    rng = np.random.default_rng(9300)
+    out = torch.full((wl.batch, wl.query_heads, wl.head_dim), float("nan"), device="cuda")
+    counter_bytes = 3 * 1024 * 4     # the workspace's tail: counters for 1024 workgroups
+
+    def call(dst):
+        if entry == "pa_decode":
+            dec(dev.q, dev.k, dev.v, dev.bt, dev.ctx, wl.scale, out=dst)
+        else:
+            pa.pa_decode_noalloc(dec.handle, dev.q.data_ptr(), dev.k.data_ptr(), dev.v.data_ptr(),
+                                 dev.bt.data_ptr(), dev.ctx.data_ptr(), wl.scale, dst.data_ptr(),
+                                 torch.cuda.current_stream().cuda_stream)
+    try:
+        assert dec.workspace is not None
+        g = _capture(lambda: call(out))
+        for rep in range(4):
+            q_new = rng.standard_normal(wl.query.shape).astype(np.float16)
+            ctx_new = np.minimum(wl.context_lengths,
+                                 rng.integers(0, int(wl.context_lengths.max()) + 1, size=wl.batch))
+            ctx_new[rep % wl.batch] = 0
+            ctx_new = ctx_new.astype(np.int32)
+            C.say(f"[case] single-launch graph replay {rep} ({entry})")
+            dev.q.copy_(torch.from_numpy(q_new))
+            dev.ctx.copy_(torch.from_numpy(ctx_new))
+            out.fill_(float("nan"))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            got = out.clone()
+            if entry == "pa_decode":
+                cnt = dec.workspace[-counter_bytes:].cpu().numpy().view(np.int32)
+                assert not cnt.any(), f"replay {rep}: arrival counters left non-zero"
+            ref = torch.full_like(out, float("nan"))
+            call(ref)
+            torch.cuda.synchronize()
+            assert torch.equal(_bits(got), _bits(ref)), f"replay {rep} differs from the eager call"
+            if rep in (0, 3):
+                exp = oracle.attend(q_new, wl.key_cache, wl.value_cache, wl.block_tables, ctx_new,
+                                    wl.scale, nthreads=C.oracle_threads())
+                C.check_against_oracle(got.cpu().numpy(), exp, f"single-launch graph replay {rep}")
+    finally:
+        dec.close()

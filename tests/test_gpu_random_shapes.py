@@ -74,3 +74,39 @@ def test_random_shape_fixed_partitions(case):
     wl = W.make_workload(name=f"random{case}", pool="holes10", seed=9950 + case, **d)
     C.decode_and_check(wl, partition_size=pages * d["page_size"],
                        what=f"random case {case}, partition of {pages} pages")
+
+
+@pytest.mark.parametrize("case", range(1, N_CASES, 2))
+def test_random_shape_single_launch(case):
+    """The same draws with the merge folded into the decode launch (PA_FLAG_SINGLE_LAUNCH):
+    bands crossing workgroups of every span the draws give."""
+    d = _draw(9900 + case)
+    wl = W.make_workload(name=f"random{case}", pool="holes10", seed=9950 + case, **d)
+    C.decode_and_check(wl, partition_size=0, flags=pa.PA_FLAG_SINGLE_LAUNCH,
+                       what=f"random case {case}, single launch")
+
+
+@pytest.mark.parametrize("case", range(0, N_CASES, 3))
+def test_random_shape_debug_bounds(case):
+    """PA_FLAG_DEBUG_BOUNDS on valid tables: the output is unchanged and the bitmap of
+    out-of-pool entries equals the oracle's (all clear)."""
+    import torch
+    d = _draw(9900 + case)
+    wl = W.make_workload(name=f"random{case}", pool="holes10", seed=9950 + case, **d)
+    C.say(f"[case] random case {case}, debug bounds: {wl.summary()}")
+    dev = C.Device(wl)
+    plain = pa.decoder_for(wl, partition_size=0)
+    dbg = pa.decoder_for(wl, partition_size=0, flags=pa.PA_FLAG_DEBUG_BOUNDS)
+    try:
+        want = dev.run(plain).clone()
+        got = dev.run(dbg).clone()
+        torch.cuda.synchronize()
+        assert torch.equal(want.view(torch.int32), got.view(torch.int32))
+        bitmap = dbg.bad_entry_bitmap()
+    finally:
+        plain.close()
+        dbg.close()
+    exp_bitmap, count = C.oracle.bad_entries(wl.block_tables, wl.context_lengths, wl.page_size,
+                                             wl.num_pages)
+    assert count == 0
+    assert np.array_equal(bitmap[:len(exp_bitmap)], np.asarray(exp_bitmap, dtype=np.uint32))
