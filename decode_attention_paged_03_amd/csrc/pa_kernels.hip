@@ -1098,8 +1098,17 @@ __device__ __forceinline__ void single_launch_merge(const DecodeArgs& a, int w, 
     }
 }
 
-// BANDWG: one workgroup per (sequence, band) -- the plan's choice for short bands.
-template <int D, int HP, int DEPTH, int NW, bool SPLIT, bool KROW, bool BANDWG>
+// How a call of the balanced route is organised (a template argument, so that the default
+// kernel carries no code of the other two):
+//   kModeSplit : the even split; crossing bands leave pieces for pa_merge_balanced;
+//   kModeBand  : one workgroup per (sequence, band) -- the plan's choice for short bands;
+//   kModeSingle: the even split, crossing bands merged by their own workgroups at the end
+//                (PA_FLAG_SINGLE_LAUNCH).
+constexpr int kModeSplit = 0;
+constexpr int kModeBand = 1;
+constexpr int kModeSingle = 2;
+
+template <int D, int HP, int DEPTH, int NW, bool SPLIT, bool KROW, int MODE>
 __global__ void __launch_bounds__(NW * 64)
 pa_decode_balanced(DecodeArgs a) {
     using G = Geo<D>;
@@ -1157,7 +1166,7 @@ pa_decode_balanced(DecodeArgs a) {
     const int NWG = gridDim.x;
     // One workgroup per (sequence, band) when every band is short (the plan's choice): the
     // workgroup's units are exactly its band's, so every stream is finished here.
-    constexpr bool bandwg = BANDWG;
+    constexpr bool bandwg = MODE == kModeBand;
     const int w = bandwg ? (int)blockIdx.x : PA_XCD_REMAP ? xcd_major((int)blockIdx.x, NWG) : (int)blockIdx.x;
     const int wb = w / SG;                    // band mode: the sequence and band of this workgroup
     const int wband = w - wb * SG;
@@ -1546,7 +1555,7 @@ pa_decode_balanced(DecodeArgs a) {
             }
         }
     }
-    if (a.single_launch) single_launch_merge<D, HP, NT>(a, w, NWG, SPW, s_rec, s_last);
+    if constexpr (MODE == kModeSingle) single_launch_merge<D, HP, NT>(a, w, NWG, SPW, s_rec, s_last);
 }
 
 // Merge of the balanced route.  Workgroup w of the decode kernel owns the band that
@@ -1860,13 +1869,16 @@ hipError_t launch_balanced_nw(const Plan& pl, const DecodeArgs& args, int ws_slo
     // (the staging is per wave: with 16 waves it would not fit next to the partial slots)
     constexpr bool kRow = PA_KROW && D == 128 && NW <= 12;
     const size_t lds = (size_t)(2 * pl.prob.batch + 1) * sizeof(int);
-    static const size_t row_static = static_lds_bytes(pa_decode_balanced<D, HP, kBalDepth, NW, SPLIT, kRow, false>);
+    static const size_t row_static = static_lds_bytes(pa_decode_balanced<D, HP, kBalDepth, NW, SPLIT, kRow, kModeSplit>);
     const bool use_row = row_static != SIZE_MAX && row_static + lds <= kLdsPerWorkgroup;
-    const auto kern = pl.band_per_wg
-                          ? (use_row ? pa_decode_balanced<D, HP, kBalDepth, NW, SPLIT, kRow, true>
-                                     : pa_decode_balanced<D, HP, kBalDepth, NW, SPLIT, false, true>)
-                          : (use_row ? pa_decode_balanced<D, HP, kBalDepth, NW, SPLIT, kRow, false>
-                                     : pa_decode_balanced<D, HP, kBalDepth, NW, SPLIT, false, false>);
+    const auto pick = [&](auto mode) {
+        constexpr int M = decltype(mode)::value;
+        return use_row ? pa_decode_balanced<D, HP, kBalDepth, NW, SPLIT, kRow, M>
+                       : pa_decode_balanced<D, HP, kBalDepth, NW, SPLIT, false, M>;
+    };
+    const auto kern = pl.band_per_wg ? pick(IntC<kModeBand>())
+                      : args.single_launch ? pick(IntC<kModeSingle>())
+                                           : pick(IntC<kModeSplit>());
     const int grid = pl.band_per_wg ? pl.prob.batch * pl.bands : balanced_grid();
     if (grid <= 0) return hipErrorInvalidDevice;
     if (!pl.band_per_wg && grid > ws_slots) return hipErrorInvalidValue;   // the workspace holds fewer workgroups' rows
