@@ -795,10 +795,39 @@ pa_merge_rows_kernel(MergeArgs a, int rows) {
 // workgroup in the workspace for the merge kernel.
 // ------------------------------------------------------------------------------------
 
+// Inclusive sum over the 64 lanes of a wave: shifts by 1, 2, 4 and 8 lanes within each row
+// of 16 (zeros shifted in), then row 0's last lane added to row 1, and lane 31's total to
+// rows 2 and 3 (rows 1 and 3 already hold rows 0 and 2).  All DPP moves on the VALU.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);   // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15, rows 1, 3
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31, rows 2, 3
+    return x;
+}
+
 // Lengths -> LDS, exclusive prefix sums of tiles per sequence.  Every thread of the
-// block calls it; returns the total tile count of one band plane.
+// block calls it; returns the total tile count of one band plane.  Up to 64 sequences,
+// every wave computes the whole prefix itself (one length per lane, a DPP scan) and
+// writes the same values: no barrier, and a wave reads what it wrote.  Callers must
+// therefore not count on a barrier here.
 template <int NT>
 __device__ __forceinline__ int tile_prefix(const int32_t* ctx, int B, int* s_pref, int* s_ctx, int* s_wsum) {
+    if (B <= 64) {
+        const int lane = threadIdx.x & 63;
+        const int c = lane < B ? ctx[lane] : 0;
+        const int mine = (c + 15) >> 4;
+        const int incl = wave_incl_scan(mine);
+        const int total = __builtin_amdgcn_readlane(incl, 63);
+        if (lane < B) {
+            s_ctx[lane] = c;
+            s_pref[lane] = incl - mine;
+        }
+        if (lane == 0) s_pref[B] = total;
+        return total;
+    }
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -1152,10 +1181,15 @@ pa_decode_balanced(DecodeArgs a) {
     const int sp = wave - rr * SPW;           // this wave's stream within a band
     const int li = sp * RW + rr;
 
-    if (tid < NS) {
-        s_meta[tid][0] = -1;
-        s_meta[tid][2] = -1;
-        s_arr[tid] = 0;
+    // each wave starts its own two slots empty (the prefix below has no barrier for
+    // small batches); the arrival counts of band mode, read by every wave, get one
+    if (L.lane < 2) {
+        s_meta[2 * li + L.lane][0] = -1;
+        s_meta[2 * li + L.lane][2] = -1;
+    }
+    if constexpr (MODE == kModeBand) {
+        if (tid < NS) s_arr[tid] = 0;
+        __syncthreads();
     }
     const int plane = tile_prefix<NT>(a.ctx, B, s_pref, s_ctx, s_wsum);
 
