@@ -1152,10 +1152,10 @@ pa_decode_balanced(DecodeArgs a) {
     __shared__ float s_m[NS][HP];
     __shared__ float s_l[NS][HP];
     __shared__ float4_t s_acc[NS][HP][C4];
-    __shared__ int s_meta[NS][3];    // stream id (-1: empty), first unit, end unit
+    // per slot: {stream id (-1: empty), first unit, end unit, band's first unit},
+    // {band's end unit, first output row, stream within the band, -}
+    __shared__ int4 s_meta[NS][2];
     __shared__ int s_arr[NS];        // one workgroup per band: arrivals at each run of pieces
-    __shared__ int s_runs[NS + 1];   // first slot of each run of one stream's slots, then NS
-    __shared__ int s_nruns;
     __shared__ int4 s_rec[2];        // the workgroup's merge records (own band, covering band)
     __shared__ int s_last[4];        // single launch: whether this workgroup merges (per stage)
     __shared__ uint4 s_kt[KROW ? NW * 16 * kKtStride : 1];   // whole-row K staging, per wave
@@ -1183,10 +1183,7 @@ pa_decode_balanced(DecodeArgs a) {
 
     // each wave starts its own two slots empty (the prefix below has no barrier for
     // small batches); the arrival counts of band mode, read by every wave, get one
-    if (L.lane < 2) {
-        s_meta[2 * li + L.lane][0] = -1;
-        s_meta[2 * li + L.lane][2] = -1;
-    }
+    if (L.lane < 2) s_meta[2 * li + L.lane][0] = int4{-1, 0, -1, 0};
     if constexpr (MODE == kModeBand) {
         if (tid < NS) s_arr[tid] = 0;
         __syncthreads();
@@ -1444,12 +1441,12 @@ pa_decode_balanced(DecodeArgs a) {
                 if constexpr (MODE == kModeBand) {
                     finish_piece(d);
                 } else if (L.lane == 0) {
-                    // units of this stream's band: [SG pref[b] + band Tb, + Tb)
+                    // units of this stream's band: [SG pref[b] + band Tb, + Tb); with them,
+                    // where the run's result goes
                     const int band = d.s / SPW;
                     const int ubase = SG * s_pref[d.b] + band * d.T;
-                    s_meta[slot][0] = d.b * S + d.s;
-                    s_meta[slot][1] = ubase + seg_lt0;
-                    s_meta[slot][2] = ubase + d.lt + 1;
+                    s_meta[slot][0] = int4{d.b * S + d.s, ubase + seg_lt0, ubase + d.lt + 1, ubase};
+                    s_meta[slot][1] = int4{ubase + d.T, (int)row0, sp, 0};
                 }
             }
         }
@@ -1559,40 +1556,44 @@ pa_decode_balanced(DecodeArgs a) {
         // outstanding into registers the compiler may reuse; otherwise it inserts waits
         // into every iteration.)
         if (PA_BAL_PRIO) set_wave_priority(0);
+    } else if constexpr (MODE != kModeBand) {
+        // no tiles: empty slots, and the records from the last wave all the same
+        clear_my_slots();
+        if (wave == NW - 1) write_records();
     }
     // One workgroup per band: every run was folded by its last wave; nothing is left.
     if constexpr (MODE == kModeBand) return;
     __syncthreads();
 
     // Runs of slots: the non-empty slots of one stream are adjacent (waves of one stream
-    // are adjacent, slots are in unit order and a band's units are contiguous).  Wave 0
-    // finds where each run starts.
-    if (wave == 0) {
+    // are adjacent, slots are in unit order and a band's units are contiguous).  Every
+    // wave finds the run starts itself -- a ballot of the filled slots, each slot's
+    // nearest filled neighbour below, a ballot of the starts -- so no barrier follows.
+    // Run r spans slots [its start, the next start), or up to NS for the last.
+    uint64_t run_starts;
+    {
         const int lane = L.lane;
-        const int sid = lane < NS ? s_meta[lane][0] : -1;
-        int last = sid;   // stream of the nearest non-empty slot at or below this one
+        const int sid = lane < NS ? s_meta[lane][0].x : -1;
+        const uint64_t filled = __builtin_amdgcn_ballot_w64(sid >= 0);
+        const uint64_t below = filled & ((1ull << lane) - 1ull);
+        const int pidx = below ? 63 - __builtin_clzll(below) : 0;
+        const int prev_sid = __shfl(sid, pidx);
+        run_starts = __builtin_amdgcn_ballot_w64(sid >= 0 && (below == 0 || sid != prev_sid));
+    }
+    const int nr = __popcll(run_starts);
+    // first slot of run r (< nr): the r-th set bit of run_starts, by halving
+    auto run_slot = [&](int r) {
+        int pos = 0;
 #pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int y = __shfl_up(last, off);
-            if (last < 0 && lane >= off) last = y;
+        for (int wdt = 32; wdt >= 1; wdt >>= 1) {
+            const int c = __popcll((run_starts >> pos) & ((1ull << wdt) - 1ull));
+            if (c <= r) {
+                r -= c;
+                pos += wdt;
+            }
         }
-        int prev = __shfl_up(last, 1);
-        if (lane == 0) prev = -1;
-        const bool start = sid >= 0 && sid != prev;
-        const uint64_t bal = __builtin_amdgcn_ballot_w64(start);
-        const int idx = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
-                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-        const int nr = __popcll(bal);
-        if (start) s_runs[idx] = lane;
-        if (lane == 0) {
-            s_runs[nr] = NS;
-            s_nruns = nr;
-        }
-    }
-    if (nk == 0) {
-        clear_my_slots();
-        if (wave == NW - 1 && !bandwg) write_records();
-    }
+        return pos;
+    };
     if (g1 == g0 && !bandwg) {
         // no units: empty triples (weight 0) for a merge whose band spans this
         // workgroup's (empty) range
@@ -1607,7 +1608,6 @@ pa_decode_balanced(DecodeArgs a) {
             }
         }
     }
-    __syncthreads();
 
     // Combine each run: HP * C4 threads per run, as many runs at once as the block holds.
     // A stream covered entirely is finished; otherwise it crosses a workgroup boundary and
@@ -1616,16 +1616,18 @@ pa_decode_balanced(DecodeArgs a) {
     constexpr int PER = HP * C4;
     constexpr int RPAR = NT / PER;
     static_assert(RPAR >= 1, "a run needs HP * D / 4 threads");
-    const int nr = s_nruns;
     const int rsub = tid / PER;
     if (rsub < RPAR) {
         const int e = tid - rsub * PER;
         const int h = e / C4;
         const int d4 = e - h * C4;
         for (int r = rsub; r < nr; r += RPAR) {
-            const int s0 = s_runs[r], s1 = s_runs[r + 1];
-            const int sid = s_meta[s0][0];
-            const int tb = s_meta[s0][1];
+            const int s0 = run_slot(r);
+            const uint64_t above = s0 < 63 ? run_starts & ~((2ull << s0) - 1ull) : 0ull;
+            const int s1 = above ? __builtin_ctzll(above) : NS;
+            const int4 m0 = s_meta[s0][0];
+            const int4 m1 = s_meta[s0][1];
+            const int tb = m0.y;
             int te = -1;
             float M = -INFINITY;
             float Ls = 0.f;
@@ -1644,7 +1646,7 @@ pa_decode_balanced(DecodeArgs a) {
                     mk[k] = in ? s_m[sl][h] : -INFINITY;
                     lk[k] = s_l[sl][h];
                     ak[k] = s_acc[sl][h][d4];
-                    te = max(te, in ? s_meta[sl][2] : -1);
+                    te = max(te, in ? s_meta[sl][0].z : -1);
                     M = fmaxf(M, mk[k]);
                 }
 #pragma unroll
@@ -1661,7 +1663,7 @@ pa_decode_balanced(DecodeArgs a) {
             } else {
                 for (int sl = s0; sl < s1; ++sl) {
                     M = fmaxf(M, s_m[sl][h]);
-                    te = max(te, s_meta[sl][2]);
+                    te = max(te, s_meta[sl][0].z);
                 }
                 for (int sl = s0; sl < s1; ++sl) {
                     const float f = fast_exp2(s_m[sl][h] - M);
@@ -1669,16 +1671,10 @@ pa_decode_balanced(DecodeArgs a) {
                     o += f * s_acc[sl][h][d4];
                 }
             }
-            const int b = sid / S;
-            const int strm = sid - b * S;
-            const int band = strm / SPW;
-            const int spr = strm - band * SPW;
-            const int Tb = s_pref[b + 1] - s_pref[b];
-            const int U0 = SG * s_pref[b] + band * Tb;
-            const int kvh = strm / a.n_chunks;
-            const int chunk = strm - kvh * a.n_chunks;
-            const size_t row0 = (size_t)b * a.query_heads + kvh * a.group + chunk * HP;
-            if (tb == U0 && te == U0 + Tb) {
+            const int U0 = m0.w;
+            const int spr = m1.z;
+            const size_t row0 = (size_t)m1.y;
+            if (tb == U0 && te == m1.x) {
                 reinterpret_cast<float4_t*>(a.out + (row0 + h) * D)[d4] = o / Ls;
             } else if (!bandwg) {   // (a band held by one workgroup is always complete)
                 const size_t wrow = (((size_t)w * 2 + (tb == g0 ? 0 : 1)) * SPW + spr) * HP + h;
