@@ -1570,11 +1570,11 @@ pa_decode_balanced(DecodeArgs a) {
     // wave finds the run starts itself -- a ballot of the filled slots, each slot's
     // nearest filled neighbour below, a ballot of the starts -- so no barrier follows.
     // Run r spans slots [its start, the next start), or up to NS for the last.
-    uint64_t run_starts;
+    uint64_t run_starts, filled;
     {
         const int lane = L.lane;
         const int sid = lane < NS ? s_meta[lane][0].x : -1;
-        const uint64_t filled = __builtin_amdgcn_ballot_w64(sid >= 0);
+        filled = __builtin_amdgcn_ballot_w64(sid >= 0);
         const uint64_t below = filled & ((1ull << lane) - 1ull);
         const int pidx = below ? 63 - __builtin_clzll(below) : 0;
         const int prev_sid = __shfl(sid, pidx);
@@ -1632,17 +1632,20 @@ pa_decode_balanced(DecodeArgs a) {
             float M = -INFINITY;
             float Ls = 0.f;
             float4_t o = {0.f, 0.f, 0.f, 0.f};
-            // Runs of up to 6 or 12 slots (two per wave; three or six waves per stream) are
-            // read all at once; empty slots inside the run fold in with weight 0, and lanes
-            // past the run's end re-read its first slot with weight 0.
+            // The run's filled slots (one per wave holding a piece; the slots between them
+            // are empty) are read all at once, 3, 6 or 12 at a time; past the last, the
+            // first is re-read with weight 0.
+            uint64_t fm = filled & (s1 >= 64 ? ~0ull : (1ull << s1) - 1ull) & ~((1ull << s0) - 1ull);
+            const int nf = __popcll(fm);
             auto fold_slots = [&](auto kf) {
                 constexpr int KF = decltype(kf)::value;
                 float mk[KF], lk[KF];
                 float4_t ak[KF];
 #pragma unroll
                 for (int k = 0; k < KF; ++k) {
-                    const bool in = s0 + k < s1;
-                    const int sl = in ? s0 + k : s0;
+                    const bool in = k < nf;
+                    const int sl = in ? __builtin_ctzll(fm) : s0;
+                    fm &= fm - 1ull;
                     mk[k] = in ? s_m[sl][h] : -INFINITY;
                     lk[k] = s_l[sl][h];
                     ak[k] = s_acc[sl][h][d4];
@@ -1656,16 +1659,20 @@ pa_decode_balanced(DecodeArgs a) {
                     o += f * ak[k];
                 }
             };
-            if (s1 - s0 <= 6) {
+            if (nf <= 3) {
+                fold_slots(IntC<3>());
+            } else if (nf <= 6) {
                 fold_slots(IntC<6>());
-            } else if (s1 - s0 <= 12) {
+            } else if (nf <= 12) {
                 fold_slots(IntC<12>());
-            } else {
-                for (int sl = s0; sl < s1; ++sl) {
+            } else {   // (more than 12 waves per stream)
+                for (uint64_t mm = fm; mm; mm &= mm - 1ull) {
+                    const int sl = __builtin_ctzll(mm);
                     M = fmaxf(M, s_m[sl][h]);
                     te = max(te, s_meta[sl][0].z);
                 }
-                for (int sl = s0; sl < s1; ++sl) {
+                for (uint64_t mm = fm; mm; mm &= mm - 1ull) {
+                    const int sl = __builtin_ctzll(mm);
                     const float f = fast_exp2(s_m[sl][h] - M);
                     Ls += f * s_l[sl][h];
                     o += f * s_acc[sl][h][d4];
