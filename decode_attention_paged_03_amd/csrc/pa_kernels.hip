@@ -588,10 +588,11 @@ constexpr int kMergeThreads = 512;
 // Balanced route: the merge tasks of a band (one row, kSliceCols float4 columns: 128
 // bytes) are dealt over the blocks of the workgroups the band spans.  In a band of at most
 // kShortMerge pieces one thread loads all pieces of its column; in longer bands a thread
-// takes kLongUnroll of them.
+// takes kLongUnroll of them (4 measured faster than 8 or 2 on a 128-piece band: more
+// threads share a task's loads, and the extra combining goes through LDS in one step).
 constexpr int kShortMerge = 16;
 constexpr int kSliceCols = 8;
-constexpr int kLongUnroll = 8;
+constexpr int kLongUnroll = 4;
 // a lane offset past every merge resource (at most 2^31 - 2^24 bytes, so that adding a
 // piece offset cannot wrap past 2^32)
 constexpr uint32_t kPastRange = 0x7F000000u;
