@@ -523,9 +523,12 @@ def measure(W, pa, wl, args, stream, steps, warmup, append_steps=0, copy_calibra
         vs.append(v0.clone())
     out = torch.empty((wl.batch, wl.query_heads, wl.head_dim), dtype=torch.float32, device=dev)
 
+    # one bound call per pool copy: arguments checked and converted once, as a decode loop
+    # would (the per-call Python checks would otherwise limit the smallest workloads)
+    calls = [dec.bind(q, ks[j], vs[j], bt, ctx, wl.scale, out, stream=stream) for j in range(n_copies)]
+
     def step(i):
-        j = i % n_copies
-        dec(q, ks[j], vs[j], bt, ctx, wl.scale, out=out, stream=stream)
+        calls[i % n_copies]()
 
     for i in range(warmup):
         step(i)

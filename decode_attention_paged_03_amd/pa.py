@@ -155,6 +155,41 @@ class PagedDecoder:
 
     def __call__(self, query, key_cache, value_cache, block_tables, context_lengths, scale,
                  out=None, stream=None):
+        out, stream = self._check(query, key_cache, value_cache, block_tables, context_lengths,
+                                  out, stream)
+        ws = self.workspace
+        pa_decode(self.handle, query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+                  block_tables.data_ptr(), context_lengths.data_ptr(), scale, out.data_ptr(),
+                  ws.data_ptr() if ws is not None else 0, self.workspace_bytes, stream.cuda_stream)
+        return out
+
+    def bind(self, query, key_cache, value_cache, block_tables, context_lengths, scale, out,
+             stream=None):
+        """The same call with its arguments checked and converted once: returns a function
+        of no arguments that enqueues pa_decode on these buffers (whose contents may change
+        between calls), for loops that repeat one decode step.  It keeps the tensors alive;
+        calling it after close() raises."""
+        out, stream = self._check(query, key_cache, value_cache, block_tables, context_lengths,
+                                  out, stream)
+        ws = self.workspace
+        P = ctypes.c_void_p
+        fn = load().pa_decode
+        args = (self.handle, P(query.data_ptr()), P(key_cache.data_ptr()), P(value_cache.data_ptr()),
+                P(block_tables.data_ptr()), P(context_lengths.data_ptr()), ctypes.c_float(scale),
+                P(out.data_ptr()), P(ws.data_ptr() if ws is not None else None),
+                ctypes.c_size_t(self.workspace_bytes), P(stream.cuda_stream))
+        keep = (query, key_cache, value_cache, block_tables, context_lengths, out, ws, stream)
+
+        def call():
+            if self.handle is None:
+                raise ValueError("the decoder was closed")
+            st = fn(*args)
+            if st != PA_OK:
+                raise PaError(st, "pa_decode")
+            return keep[5]
+        return call
+
+    def _check(self, query, key_cache, value_cache, block_tables, context_lengths, out, stream):
         import torch
         p = self.problem
         for name, t, dt in (("query", query, torch.float16), ("key_cache", key_cache, torch.float16),
@@ -180,11 +215,7 @@ class PagedDecoder:
             raise ValueError("out: need a contiguous float32 [batch][query_heads][head_dim] tensor")
         if stream is None:
             stream = torch.cuda.current_stream(query.device)
-        ws = self.workspace
-        pa_decode(self.handle, query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
-                  block_tables.data_ptr(), context_lengths.data_ptr(), scale, out.data_ptr(),
-                  ws.data_ptr() if ws is not None else 0, self.workspace_bytes, stream.cuda_stream)
-        return out
+        return out, stream
 
     def bad_entry_bitmap(self):
         """With PA_FLAG_DEBUG_BOUNDS: the bitmap the last call left at the start of the

@@ -210,3 +210,31 @@ def test_page_relabel_bitwise(partition):
         finally:
             dec.close()
     assert torch.equal(outs[0].view(torch.int32), outs[1].view(torch.int32))
+
+
+def test_bound_call_same_bits():
+    """PagedDecoder.bind: the arguments checked once, then repeated calls on the same
+    buffers.  Each call equals the checked call bit for bit, sees new buffer contents, and
+    a call after close() raises instead of reaching the library."""
+    import torch
+    wl = W.make_named("small_batch")
+    dev = C.Device(wl)
+    dec = pa.decoder_for(wl)
+    out = torch.full((wl.batch, wl.query_heads, wl.head_dim), float("nan"), device="cuda")
+    try:
+        call = dec.bind(dev.q, dev.k, dev.v, dev.bt, dev.ctx, wl.scale, out)
+        rng = np.random.default_rng(9500)
+        for rep in range(3):
+            C.say(f"[case] bound call {rep}")
+            dev.q.copy_(torch.from_numpy(rng.standard_normal(wl.query.shape).astype(np.float16)))
+            out.fill_(float("nan"))
+            call()
+            ref = dec(dev.q, dev.k, dev.v, dev.bt, dev.ctx, wl.scale)
+            torch.cuda.synchronize()
+            assert torch.equal(out.view(torch.int32), ref.view(torch.int32)), rep
+        with pytest.raises(ValueError):
+            dec.bind(dev.q, dev.k, dev.v, dev.bt, dev.ctx[:1], wl.scale, out)
+    finally:
+        dec.close()
+    with pytest.raises(ValueError):
+        call()
