@@ -1610,18 +1610,24 @@ pa_decode_balanced(DecodeArgs a) {
         }
     }
 
-    // Combine each run: HP * C4 threads per run, as many runs at once as the block holds.
-    // A stream covered entirely is finished; otherwise it crosses a workgroup boundary and
-    // its triple goes to the workspace: side 0 for the band holding the workgroup's first
-    // unit, side 1 for the one holding its last unit.
-    constexpr int PER = HP * C4;
-    constexpr int RPAR = NT / PER;
-    static_assert(RPAR >= 1, "a run needs HP * D / 4 threads");
-    const int rsub = tid / PER;
-    if (rsub < RPAR) {
-        const int e = tid - rsub * PER;
-        const int h = e / C4;
-        const int d4 = e - h * C4;
+    // Combine each run: HP * C4 / EPT threads per run, EPT float4 elements each, as many
+    // runs at once as the block holds.  A stream covered entirely is finished; otherwise it
+    // crosses a workgroup boundary and its triple goes to the workspace: side 0 for the
+    // band holding the workgroup's first unit, side 1 for the one holding its last unit.
+    auto combine = [&](auto ept) {
+        constexpr int EPT = decltype(ept)::value;
+        constexpr int PER = HP * C4 / EPT;
+        constexpr int RPAR = NT / PER;
+        static_assert(PER * EPT == HP * C4 && RPAR >= 1, "a run needs HP * D / 4 / EPT threads");
+        const int rsub = tid / PER;
+        if (rsub >= RPAR) return;
+        int h[EPT], d4[EPT];
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) {
+            const int e = tid - rsub * PER + j * PER;
+            h[j] = e / C4;
+            d4[j] = e - h[j] * C4;
+        }
         for (int r = rsub; r < nr; r += RPAR) {
             const int s0 = run_slot(r);
             const uint64_t above = s0 < 63 ? run_starts & ~((2ull << s0) - 1ull) : 0ull;
@@ -1630,69 +1636,108 @@ pa_decode_balanced(DecodeArgs a) {
             const int4 m1 = s_meta[s0][1];
             const int tb = m0.y;
             int te = -1;
-            float M = -INFINITY;
-            float Ls = 0.f;
-            float4_t o = {0.f, 0.f, 0.f, 0.f};
+            float M[EPT], Ls[EPT];
+            float4_t o[EPT];
+#pragma unroll
+            for (int j = 0; j < EPT; ++j) {
+                M[j] = -INFINITY;
+                Ls[j] = 0.f;
+                o[j] = float4_t{0.f, 0.f, 0.f, 0.f};
+            }
             // The run's filled slots (one per wave holding a piece; the slots between them
             // are empty) are read all at once, 3, 6 or 12 at a time; past the last, the
             // first is re-read with weight 0.
-            uint64_t fm = filled & (s1 >= 64 ? ~0ull : (1ull << s1) - 1ull) & ~((1ull << s0) - 1ull);
-            const int nf = __popcll(fm);
+            const uint64_t fm0 = filled & (s1 >= 64 ? ~0ull : (1ull << s1) - 1ull) & ~((1ull << s0) - 1ull);
+            const int nf = __popcll(fm0);
             auto fold_slots = [&](auto kf) {
                 constexpr int KF = decltype(kf)::value;
-                float mk[KF], lk[KF];
-                float4_t ak[KF];
+                uint64_t fm = fm0;
+                int sl[KF];
 #pragma unroll
                 for (int k = 0; k < KF; ++k) {
-                    const bool in = k < nf;
-                    const int sl = in ? __builtin_ctzll(fm) : s0;
+                    sl[k] = k < nf ? __builtin_ctzll(fm) : s0;
                     fm &= fm - 1ull;
-                    mk[k] = in ? s_m[sl][h] : -INFINITY;
-                    lk[k] = s_l[sl][h];
-                    ak[k] = s_acc[sl][h][d4];
-                    te = max(te, in ? s_meta[sl][0].z : -1);
-                    M = fmaxf(M, mk[k]);
+                    te = max(te, k < nf ? s_meta[sl[k]][0].z : -1);
                 }
 #pragma unroll
-                for (int k = 0; k < KF; ++k) {
-                    const float f = fast_exp2(mk[k] - M);
-                    Ls += f * lk[k];
-                    o += f * ak[k];
+                for (int j = 0; j < EPT; ++j) {
+                    float mk[KF], lk[KF];
+                    float4_t ak[KF];
+#pragma unroll
+                    for (int k = 0; k < KF; ++k) {
+                        mk[k] = k < nf ? s_m[sl[k]][h[j]] : -INFINITY;
+                        lk[k] = s_l[sl[k]][h[j]];
+                        ak[k] = s_acc[sl[k]][h[j]][d4[j]];
+                        M[j] = fmaxf(M[j], mk[k]);
+                    }
+#pragma unroll
+                    for (int k = 0; k < KF; ++k) {
+                        const float f = fast_exp2(mk[k] - M[j]);
+                        Ls[j] += f * lk[k];
+                        o[j] += f * ak[k];
+                    }
                 }
             };
+            // (a thread holds at most 12 slots: with 2 or 4 elements it is never given runs
+            // of more than 6 or 3 filled slots, and those folds are not compiled)
+            bool done = false;
             if (nf <= 3) {
                 fold_slots(IntC<3>());
-            } else if (nf <= 6) {
-                fold_slots(IntC<6>());
-            } else if (nf <= 12) {
-                fold_slots(IntC<12>());
-            } else {   // (more than 12 waves per stream)
-                for (uint64_t mm = fm; mm; mm &= mm - 1ull) {
-                    const int sl = __builtin_ctzll(mm);
-                    M = fmaxf(M, s_m[sl][h]);
-                    te = max(te, s_meta[sl][0].z);
+                done = true;
+            }
+            if constexpr (EPT <= 2) {
+                if (!done && nf <= 6) {
+                    fold_slots(IntC<6>());
+                    done = true;
                 }
-                for (uint64_t mm = fm; mm; mm &= mm - 1ull) {
-                    const int sl = __builtin_ctzll(mm);
-                    const float f = fast_exp2(s_m[sl][h] - M);
-                    Ls += f * s_l[sl][h];
-                    o += f * s_acc[sl][h][d4];
+            }
+            if constexpr (EPT == 1) {
+                if (!done && nf <= 12) {
+                    fold_slots(IntC<12>());
+                    done = true;
+                }
+            }
+            if (!done) {   // (more than 12 waves per stream)
+                for (uint64_t mm = fm0; mm; mm &= mm - 1ull) te = max(te, s_meta[__builtin_ctzll(mm)][0].z);
+#pragma unroll
+                for (int j = 0; j < EPT; ++j) {
+                    for (uint64_t mm = fm0; mm; mm &= mm - 1ull) M[j] = fmaxf(M[j], s_m[__builtin_ctzll(mm)][h[j]]);
+                    for (uint64_t mm = fm0; mm; mm &= mm - 1ull) {
+                        const int sl = __builtin_ctzll(mm);
+                        const float f = fast_exp2(s_m[sl][h[j]] - M[j]);
+                        Ls[j] += f * s_l[sl][h[j]];
+                        o[j] += f * s_acc[sl][h[j]][d4[j]];
+                    }
                 }
             }
             const int U0 = m0.w;
             const int spr = m1.z;
             const size_t row0 = (size_t)m1.y;
-            if (tb == U0 && te == m1.x) {
-                reinterpret_cast<float4_t*>(a.out + (row0 + h) * D)[d4] = o / Ls;
-            } else if (!bandwg) {   // (a band held by one workgroup is always complete)
-                const size_t wrow = (((size_t)w * 2 + (tb == g0 ? 0 : 1)) * SPW + spr) * HP + h;
-                reinterpret_cast<float4_t*>(a.ws_acc + wrow * D)[d4] = o;
-                if (d4 == 0) {
-                    a.ws_ml[wrow * 2] = M;
-                    a.ws_ml[wrow * 2 + 1] = Ls;
+            const bool complete = tb == U0 && te == m1.x;
+#pragma unroll
+            for (int j = 0; j < EPT; ++j) {
+                if (complete) {
+                    reinterpret_cast<float4_t*>(a.out + (row0 + h[j]) * D)[d4[j]] = o[j] / Ls[j];
+                } else if (!bandwg) {   // (a band held by one workgroup is always complete)
+                    const size_t wrow = (((size_t)w * 2 + (tb == g0 ? 0 : 1)) * SPW + spr) * HP + h[j];
+                    reinterpret_cast<float4_t*>(a.ws_acc + wrow * D)[d4[j]] = o[j];
+                    if (d4[j] == 0) {
+                        a.ws_ml[wrow * 2] = M[j];
+                        a.ws_ml[wrow * 2 + 1] = Ls[j];
+                    }
                 }
             }
         }
+    };
+    // Elements per thread: one, unless the runs outnumber the block's run groups; then 2 or
+    // 4, so that every run is folded in one pass, as long as a thread holds at most 12
+    // slots of pieces (a run has one filled slot per wave of its stream).
+    {
+        constexpr int RPAR1 = NT / (HP * C4);
+        const int kfmax = RW <= 3 ? 3 : RW <= 6 ? 6 : 12;
+        if (nr > RPAR1 && NT / (HP * C4 / 2) >= nr && 2 * kfmax <= 12) combine(IntC<2>());
+        else if (nr > RPAR1 && (HP * C4) % 4 == 0 && 4 * kfmax <= 12) combine(IntC<4>());
+        else combine(IntC<1>());
     }
     if constexpr (MODE == kModeSingle) single_launch_merge<D, HP, NT>(a, w, NWG, SPW, s_rec, s_last);
 }
