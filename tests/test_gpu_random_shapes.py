@@ -110,3 +110,47 @@ def test_random_shape_debug_bounds(case):
                                              wl.num_pages)
     assert count == 0
     assert np.array_equal(bitmap[:len(exp_bitmap)], np.asarray(exp_bitmap, dtype=np.uint32))
+
+
+def _draw_short(seed):
+    """A shape whose bands are all short enough for one workgroup per band: heads per
+    wave, streams and streams per band as the plan derives them, contexts up to the
+    longest band that mode takes (24 stream tiles), with empty sequences and single
+    tokens among them."""
+    import math
+    rng = np.random.default_rng(seed)
+    kv_heads = int(rng.choice([1, 2, 3, 4, 8]))
+    group = int(rng.choice([1, 2, 3, 4, 6, 8]))
+    hp = max(h for h in range(1, 9) if group % h == 0)
+    streams = kv_heads * (group // hp)
+    batch = int(rng.integers(1, 40))
+    spw = math.gcd(streams, 12)
+    if batch * (streams // spw) < 32 and spw % 2 == 0:
+        spw //= 2
+    page_size = int(rng.choice([8, 16, 32]))
+    cap = 16 * (24 // spw)                      # tokens: the longest band of this mode
+    longest = (cap // page_size) * page_size   # the table's bound must fit it too
+    ctx = rng.integers(0, longest + 1, size=batch)
+    ctx[rng.random(batch) < 0.15] = 1
+    ctx[rng.random(batch) < 0.15] = 0
+    ctx[int(rng.integers(0, batch))] = longest
+    return dict(batch=batch, query_heads=kv_heads * group, kv_heads=kv_heads,
+                head_dim=int(rng.choice([64, 128])), page_size=page_size,
+                context_lengths=[int(c) for c in ctx])
+
+
+@pytest.mark.parametrize("case", range(16))
+def test_random_short_bands(case):
+    """Seeded shapes that take one workgroup per band, where each stream's pieces are
+    folded by the last of its waves to finish one: up to 24 tiles per band, streams of 1
+    to 12 waves, waves with no tiles between others."""
+    d = _draw_short(9700 + case)
+    wl = W.make_workload(name=f"short{case}", pool="holes10", seed=9750 + case, **d)
+    dec = pa.decoder_for(wl, partition_size=0)
+    try:
+        assert dec.workspace_bytes == 0, f"case {case}: expected one workgroup per band ({d})"
+    finally:
+        dec.close()
+    C.decode_and_check(wl, partition_size=0,
+                       what=f"short bands case {case}: QH{d['query_heads']}/KVH{d['kv_heads']} "
+                            f"D{d['head_dim']} ps{d['page_size']} B{d['batch']}")
