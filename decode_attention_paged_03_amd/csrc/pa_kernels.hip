@@ -446,13 +446,18 @@ pa_decode_kernel(DecodeArgs a) {
     const Lane L = Lane::make(tid & 63);
 
     // Work item: partitions vary slowest, so every sequence's first (largest) partition
-    // is dispatched before any remainder partition.
+    // is dispatched before any remainder partition.  Workgroups are dealt to the XCDs in
+    // turn, so with the KV head varying fastest each XCD would read the same head's rows
+    // throughout; the head is rotated by sequence + partition instead (a permutation of
+    // the items of one (sequence, partition)).  Measured on partitions of 1024: batch64
+    // 77.4 -> 73.4 us, mixed128 284.6 -> 265.4 us; long100k +0.9 and small_batch +0.5 us.
     int id = blockIdx.x;
     const int chunk = id % a.n_chunks; id /= a.n_chunks;
-    const int kvh = id % a.kv_heads;   id /= a.kv_heads;
+    const int kvh_dealt = id % a.kv_heads; id /= a.kv_heads;
     const int nb = (int)(gridDim.x / (unsigned)(a.n_chunks * a.kv_heads * a.n_part_max));
     const int b = id % nb;
     const int part = id / nb;
+    const int kvh = (kvh_dealt + b + part) % a.kv_heads;
 
     const int ctx = a.ctx[b];
     const int P = a.partition;
