@@ -94,7 +94,7 @@ constexpr uint32_t kOutOfRange = 0x7FFFFF00u;
 #define PA_XCD_REMAP 1   // balanced route: contiguous work per XCD (see xcd_major)
 #endif
 #ifndef PA_KROW
-#define PA_KROW 1    // balanced route: load K in whole rows and regroup them through LDS
+#define PA_KROW 1    // load K in whole rows and regroup them through LDS (head_dim 128, both routes)
 #endif
 #ifndef PA_RUN_SKEW
 #define PA_RUN_SKEW 20   // balanced route: percent by which early rounds of waves get more work
@@ -440,6 +440,9 @@ pa_decode_kernel(DecodeArgs a) {
     __shared__ float s_m[NW][HP];
     __shared__ float s_l[NW][HP];
     __shared__ float4_t s_acc[NW][HP][C4];
+    // K in whole rows, regrouped through LDS as on the balanced route (head_dim 128)
+    constexpr bool KR = PA_KROW && D == 128;
+    __shared__ uint4 s_kt[KR ? NW * 16 * kKtStride : 1];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -491,8 +494,9 @@ pa_decode_kernel(DecodeArgs a) {
     const size_t page_bytes = tok_bytes << ps_log2;
     const char* kbase = a.k + (size_t)kvh * D * 2;
     const char* vbase = a.v + (size_t)kvh * D * 2;
-    const uint32_t koff = (uint32_t)(L.ktok * tok_bytes) + 16u * L.g;
     const uint32_t voff = (uint32_t)(L.g * tok_bytes) + 2u * G::E * L.n;
+    const uint32_t koff = KR ? voff : (uint32_t)(L.ktok * tok_bytes) + 16u * L.g;
+    uint4* const kt = KR ? &s_kt[wave * 16 * kKtStride] : nullptr;
     const float sl2 = a.scale_log2;
 
     WaveState<D, HP> st;
@@ -518,7 +522,7 @@ pa_decode_kernel(DecodeArgs a) {
                 base2 = (size_t)max(phys2, 0) * page_bytes;
             }
         }
-        load_kv<D, SPLIT>(kbase + base, vbase + base, kbase + base2, vbase + base2, koff, voff,
+        load_kv<D, SPLIT, KR>(kbase + base, vbase + base, kbase + base2, vbase + base2, koff, voff,
                           (uint32_t)tok_bytes, max(0, min(T, t_end - t0)), phys >= 0, phys2 >= 0, L,
                           kb, vb);
     };
@@ -542,7 +546,7 @@ pa_decode_kernel(DecodeArgs a) {
                 load_tile(min(k + d + DEPTH - 1, nk - 1), kb[nxt], vb[nxt]);
                 __builtin_amdgcn_sched_barrier(0);
                 const int t0 = t_begin + (wave + (k + d) * NW) * T;
-                if (k + d < nk) st.tile(qb, kb[d], vb[d], max(0, min(T, t_end - t0)), sl2, L);
+                if (k + d < nk) st.template tile<KR>(qb, kb[d], vb[d], max(0, min(T, t_end - t0)), sl2, L, kt);
                 else __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
             }
         }
