@@ -2036,6 +2036,7 @@ pa_bad_entries_kernel(const int32_t* bt, const int32_t* ctx, int max_pages, int 
 #define PA_BAL_DEPTH 1   // tile buffers per wave (balanced route)
 #endif
 constexpr int kWaves = PA_WAVES;
+constexpr int kWavesWide = 8;   // fixed route, at most one workgroup per compute unit
 constexpr int kDepth = PA_DEPTH;
 constexpr int kBalDepth = PA_BAL_DEPTH;
 
@@ -2100,12 +2101,20 @@ hipError_t launch_decode(const Plan& pl, const DecodeArgs& args, int ws_slots, h
     if (pl.balanced)
         return split ? launch_balanced<D, HP, true>(pl, args, ws_slots, stream)
                      : launch_balanced<D, HP, false>(pl, args, ws_slots, stream);
-    if (!split)
-        hipLaunchKernelGGL((pa_decode_kernel<D, HP, kDepth, kWaves, false>),
-                           dim3((unsigned)pl.decode_grid), dim3(kWaves * 64), 0, stream, args);
-    else
-        hipLaunchKernelGGL((pa_decode_kernel<D, HP, kDepth, kWaves, true>),
-                           dim3((unsigned)pl.decode_grid), dim3(kWaves * 64), 0, stream, args);
+    // Fixed partitions: with no more workgroups than compute units, 8 waves per workgroup
+    // share a partition's tiles; otherwise 4, so that more workgroups stay resident per
+    // CU.  (Partitions of 1024: small_batch, 256 workgroups, 24.7 -> 21.4 us with 8 waves;
+    // batch64, long100k and mixed128, with 2 to 16 workgroups per CU, were slower with 8.)
+    const int cus = device_compute_units();
+    const bool wide = cus > 0 && pl.decode_grid <= cus;
+    const dim3 grid((unsigned)pl.decode_grid);
+    if (wide) {
+        if (!split) hipLaunchKernelGGL((pa_decode_kernel<D, HP, kDepth, kWavesWide, false>), grid, dim3(kWavesWide * 64), 0, stream, args);
+        else hipLaunchKernelGGL((pa_decode_kernel<D, HP, kDepth, kWavesWide, true>), grid, dim3(kWavesWide * 64), 0, stream, args);
+    } else {
+        if (!split) hipLaunchKernelGGL((pa_decode_kernel<D, HP, kDepth, kWaves, false>), grid, dim3(kWaves * 64), 0, stream, args);
+        else hipLaunchKernelGGL((pa_decode_kernel<D, HP, kDepth, kWaves, true>), grid, dim3(kWaves * 64), 0, stream, args);
+    }
     return hipGetLastError();
 }
 
