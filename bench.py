@@ -486,18 +486,21 @@ def kernel_resources(kernel_names):
     return out or None
 
 
-def decode_kernel_names(wl, band_per_wg: bool):
+def decode_kernel_names(wl, short: bool, cus: int = 256):
     """Names (as in profiles/resources.txt) of the kernels one pa_decode call runs on the
-    default (balanced) route: heads per wave = the largest divisor of the group up to 8;
-    pages of 8 split a tile; whole-row K loads at head_dim 128 (when the LDS fits); with
-    short bands (one workgroup per band, no workspace) no merge kernel."""
+    library's own route: heads per wave = the largest divisor of the group up to 8; pages
+    of 8 split a tile; whole-row K loads at head_dim 128 (when the LDS fits).  Short
+    contexts (no workspace) take the fixed kernel with one partition per sequence -- 8
+    waves when its grid (batch x KV heads x head chunks) fits the compute units, else 4 --
+    and no merge."""
     hp = max(h for h in range(1, 9) if wl.group % h == 0)
     split = 1 if wl.page_size < 16 else 0
+    if short:
+        grid = wl.batch * wl.kv_heads * (wl.group // hp)
+        return [f"pa_decode_kernel<{wl.head_dim},{hp},1,{8 if grid <= cus else 4},{split}>"]
     krow = 1 if wl.head_dim == 128 else 0
-    names = [f"pa_decode_balanced<{wl.head_dim},{hp},1,12,{split},{krow},{int(band_per_wg)}>"]
-    if not band_per_wg:
-        names.append(f"pa_merge_balanced<{wl.head_dim},{hp}>")
-    return names
+    return [f"pa_decode_balanced<{wl.head_dim},{hp},1,12,{split},{krow},0>",
+            f"pa_merge_balanced<{wl.head_dim},{hp}>"]
 
 
 def measure(W, pa, wl, args, stream, steps, warmup, append_steps=0, copy_calibration=False):
@@ -571,7 +574,7 @@ def measure(W, pa, wl, args, stream, steps, warmup, append_steps=0, copy_calibra
 
     balanced = dec.problem.partition_size == 0
     if balanced and dec.workspace_bytes == 0:
-        kernel_name = "pa_decode call: pa_decode_balanced, one workgroup per band (no merge)"
+        kernel_name = "pa_decode call: pa_decode_kernel, one partition per sequence (short contexts, no merge)"
     elif balanced:
         kernel_name = "pa_decode call: pa_decode_balanced + pa_merge_balanced"
     elif fixed:
@@ -616,7 +619,8 @@ def measure(W, pa, wl, args, stream, steps, warmup, append_steps=0, copy_calibra
     }
     if balanced:
         # the default route needs no workspace only with one workgroup per band
-        res["roofline"]["resources"] = kernel_resources(decode_kernel_names(wl, dec.workspace_bytes == 0))
+        cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+        res["roofline"]["resources"] = kernel_resources(decode_kernel_names(wl, dec.workspace_bytes == 0, cus))
     if append_line:
         res["append"] = append_line
     dec.close()

@@ -32,10 +32,10 @@ constexpr size_t kNoallocCounterBytes = 64 * 1024;
 // Query heads one wave scores at once (MFMA rows are 16; LDS partial slots are sized
 // for this many heads).
 constexpr int kMaxHeadsPerWave = 8;
-// Balanced route: one workgroup per (sequence, band) when no band can hold more than this
-// many stream tiles (about two per wave of a 12-wave workgroup) and the batch's bands fit
-// the grid limit.  Such a call needs no merge launch.
-constexpr int kBandPerWgMaxTiles = 24;
+// Short contexts: when no band of the balanced route could hold more than this many stream
+// tiles (about two per wave of a 12-wave workgroup; the host's bound), every sequence is
+// one partition of the fixed route instead.  Such a call needs no merge and no workspace.
+constexpr int kShortBandTiles = 24;
 
 struct Plan {
     pa_problem prob;        // validated copy, defaults resolved
@@ -43,8 +43,8 @@ struct Plan {
     int heads_per_wg;       // query heads one workgroup serves (divides group, <= 8)
     int n_chunks;           // group / heads_per_wg
     bool balanced;          // route: even split of all token tiles over a resident grid
-    bool band_per_wg;       // balanced route, short bands: one workgroup per (sequence, band),
-                            // no merge and no workspace
+    bool short_single;      // short contexts (the host's bound): the fixed route with one
+                            // partition per sequence, no merge and no workspace
     bool partition_balanced;  // a partition size was given and the balanced route may run
                               // (when its partials fit it: balanced_partials_fit)
     long long balanced_units_max;  // balanced route: bound on the batch's (band, tile) units

@@ -1138,14 +1138,12 @@ __device__ __forceinline__ void single_launch_merge(const DecodeArgs& a, int w, 
 }
 
 // How a call of the balanced route is organised (a template argument, so that the default
-// kernel carries no code of the other two):
+// kernel carries no code of the other):
 //   kModeSplit : the even split; crossing bands leave pieces for pa_merge_balanced;
-//   kModeBand  : one workgroup per (sequence, band) -- the plan's choice for short bands;
 //   kModeSingle: the even split, crossing bands merged by their own workgroups at the end
 //                (PA_FLAG_SINGLE_LAUNCH).
 constexpr int kModeSplit = 0;
-constexpr int kModeBand = 1;
-constexpr int kModeSingle = 2;
+constexpr int kModeSingle = 1;
 
 template <int D, int HP, int DEPTH, int NW, bool SPLIT, bool KROW, int MODE>
 __global__ void __launch_bounds__(NW * 64)
@@ -1165,7 +1163,6 @@ pa_decode_balanced(DecodeArgs a) {
     // per slot: {stream id (-1: empty), first unit, end unit, band's first unit},
     // {band's end unit, first output row, stream within the band, -}
     __shared__ int4 s_meta[NS][2];
-    __shared__ int s_arr[NS];        // one workgroup per band: arrivals at each run of pieces
     __shared__ int4 s_rec[2];        // the workgroup's merge records (own band, covering band)
     __shared__ int s_last[4];        // single launch: whether this workgroup merges (per stage)
     __shared__ uint4 s_kt[KROW ? NW * 16 * kKtStride : 1];   // whole-row K staging, per wave
@@ -1192,12 +1189,8 @@ pa_decode_balanced(DecodeArgs a) {
     const int li = sp * RW + rr;
 
     // each wave starts its own two slots empty (the prefix below has no barrier for
-    // small batches); the arrival counts of band mode, read by every wave, get one
+    // small batches)
     if (L.lane < 2) s_meta[2 * li + L.lane][0] = int4{-1, 0, -1, 0};
-    if constexpr (MODE == kModeBand) {
-        if (tid < NS) s_arr[tid] = 0;
-        __syncthreads();
-    }
     const int plane = tile_prefix<NT>(a.ctx, B, s_pref, s_ctx, s_wsum);
 
     // empty sequences: a zero output, written by one workgroup each
@@ -1207,14 +1200,9 @@ pa_decode_balanced(DecodeArgs a) {
 
     const int N = SG * plane;
     const int NWG = gridDim.x;
-    // One workgroup per (sequence, band) when every band is short (the plan's choice): the
-    // workgroup's units are exactly its band's, so every stream is finished here.
-    constexpr bool bandwg = MODE == kModeBand;
-    const int w = bandwg ? (int)blockIdx.x : PA_XCD_REMAP ? xcd_major((int)blockIdx.x, NWG) : (int)blockIdx.x;
-    const int wb = w / SG;                    // band mode: the sequence and band of this workgroup
-    const int wband = w - wb * SG;
-    const int g0 = bandwg ? SG * s_pref[wb] + wband * (s_pref[wb + 1] - s_pref[wb]) : split_point(w, N, NWG);
-    const int g1 = bandwg ? g0 + (s_pref[wb + 1] - s_pref[wb]) : split_point(w + 1, N, NWG);
+    const int w = PA_XCD_REMAP ? xcd_major((int)blockIdx.x, NWG) : (int)blockIdx.x;
+    const int g0 = split_point(w, N, NWG);
+    const int g1 = split_point(w + 1, N, NWG);
     auto run_start = [&](int r) {   // cumulative weight of runs 0 .. r-1, over the total
         if (RW == 1) return r == 0 ? g0 : g1;
         const long long cum = (long long)r * (RW - 1) * (100 + PA_RUN_SKEW) - (long long)PA_RUN_SKEW * r * (r - 1);
@@ -1224,16 +1212,6 @@ pa_decode_balanced(DecodeArgs a) {
     const int wr0 = run_start(rr);
     const int wr1 = run_start(rr + 1);
     const int nk = wr1 - wr0;
-    // One workgroup per band: the start of every run's range, lane j holding run j's (j <=
-    // RW), and the runs that hold units -- the wave of a piece finds the other waves of
-    // its band from these.
-    [[maybe_unused]] int run_bnd = 0;
-    [[maybe_unused]] uint64_t run_nonempty = 0;
-    if constexpr (MODE == kModeBand) {
-        run_bnd = L.lane <= RW ? run_start(L.lane) : 0x7fffffff;
-        const int run_bnd_next = __shfl_down(run_bnd, 1);
-        run_nonempty = __builtin_amdgcn_ballot_w64(L.lane < RW && run_bnd < run_bnd_next);
-    }
 
     const int ps_log2 = a.ps_log2;
     const size_t tok_bytes = (size_t)a.kv_heads * D * 2;
@@ -1339,91 +1317,6 @@ pa_decode_balanced(DecodeArgs a) {
         if (d.first) load_q_raw<D, HP>(a.q, (size_t)cb * a.query_heads + ckvh * a.group + cchunk * HP, L, qr);
     };
 
-    // One workgroup per band: a piece is the part of the band's stream that one wave holds
-    // when the stream is spread over several waves.  Its wave stores it in its slot and
-    // counts itself in; the waves holding the stream (the runs whose ranges meet the
-    // band's units, each with one piece) all compute the same run and count, and the last
-    // to arrive folds the pieces in wave order and writes the rows.  Nothing waits: the
-    // workgroup ends when its last wave has folded what it finished, with no barrier and
-    // no combine pass: about 0.7 us less per call at short contexts.  (On the even split
-    // the combine pass below is faster: there most pieces are finished at the end anyway,
-    // and all waves folding together beat one wave folding alone.)
-    auto finish_piece = [&](const Desc& d) {
-        const int band = d.s / SPW;
-        const int U0 = SG * s_pref[d.b] + band * d.T;
-        const int lo_u = max(U0, g0), hi_u = min(U0 + d.T, g1);
-        const bool bnd_lane = L.lane >= 1 && L.lane <= RW;
-        const int rr_lo = __popcll(__builtin_amdgcn_ballot_w64(bnd_lane && run_bnd <= lo_u));
-        const int rr_hi = __popcll(__builtin_amdgcn_ballot_w64(bnd_lane && run_bnd <= hi_u - 1));
-        const uint64_t members = run_nonempty & ((2ull << rr_hi) - 1ull) & ~((1ull << rr_lo) - 1ull);
-        const int n_mem = __popcll(members);
-        // the first piece is in its wave's second slot unless the band starts that wave
-        const int side_lo = __shfl(run_bnd, rr_lo) == lo_u ? 0 : 1;
-        const int key = 2 * (sp * RW + rr_lo) + side_lo;
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the slot is written
-        int old = 0;
-        if (L.lane == 0) old = __hip_atomic_fetch_add(&s_arr[key], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        old = __builtin_amdgcn_readfirstlane(__shfl(old, 0));
-        asm volatile("" ::: "memory");
-        if (old != n_mem - 1) return;
-        // the last arrival: maximum, then weights and sums, over the pieces in wave order
-        constexpr int NE = HP * C4;
-        constexpr int EPL = (NE + 63) / 64;
-        float mx[EPL], ls[EPL];
-        float4_t ov[EPL];
-#pragma unroll
-        for (int k = 0; k < EPL; ++k) {
-            mx[k] = -INFINITY;
-            ls[k] = 0.f;
-            ov[k] = float4_t{0.f, 0.f, 0.f, 0.f};
-        }
-        for (uint64_t mm = members; mm; mm &= mm - 1) {
-            const int r2 = __builtin_ctzll(mm);
-            const int sl = 2 * (sp * RW + r2) + (r2 == rr_lo ? side_lo : 0);
-#pragma unroll
-            for (int k = 0; k < EPL; ++k) {
-                const int e = L.lane + 64 * k;
-                if (e < NE) mx[k] = fmaxf(mx[k], s_m[sl][e / C4]);
-            }
-        }
-        for (uint64_t mm = members; mm; mm &= mm - 1) {
-            const int r2 = __builtin_ctzll(mm);
-            const int sl = 2 * (sp * RW + r2) + (r2 == rr_lo ? side_lo : 0);
-#pragma unroll
-            for (int k = 0; k < EPL; ++k) {
-                const int e = L.lane + 64 * k;
-                if (e < NE) {
-                    const int h = e / C4;
-                    const float f = fast_exp2(s_m[sl][h] - mx[k]);
-                    ls[k] += f * s_l[sl][h];
-                    ov[k] += f * s_acc[sl][h][e - h * C4];
-                }
-            }
-        }
-        const int kvh = d.s / a.n_chunks;
-        const int chunk = d.s - kvh * a.n_chunks;
-        const size_t row0 = (size_t)d.b * a.query_heads + kvh * a.group + chunk * HP;
-        const bool complete = lo_u == U0 && hi_u == U0 + d.T;
-        const size_t wbase = (((size_t)w * 2 + (lo_u == g0 ? 0 : 1)) * SPW + sp) * HP;
-#pragma unroll
-        for (int k = 0; k < EPL; ++k) {
-            const int e = L.lane + 64 * k;
-            if (e >= NE) continue;
-            const int h = e / C4;
-            const int d4 = e - h * C4;
-            if (complete) {
-                reinterpret_cast<float4_t*>(a.out + (row0 + h) * D)[d4] = ov[k] / ls[k];
-            } else if (!bandwg) {   // (a band held by one workgroup is always complete)
-                const size_t wrow = wbase + h;
-                reinterpret_cast<float4_t*>(a.ws_acc + wrow * D)[d4] = ov[k];
-                if (d4 == 0) {
-                    a.ws_ml[wrow * 2] = mx[k];
-                    a.ws_ml[wrow * 2 + 1] = ls[k];
-                }
-            }
-        }
-    };
-
     WaveState<D, HP> st;
     uint4 qb[G::UK];       // B operand of the scores (with one tile buffer, also the load target)
     int seg_lt0 = 0;       // first stream tile of the open segment
@@ -1448,9 +1341,7 @@ pa_decode_balanced(DecodeArgs a) {
                 // wave's first segment, 2 wave + 1 for its last one
                 const int slot = 2 * li + (seg_i0 == 0 ? 0 : 1);
                 st.store_triple(&s_m[slot][0], &s_l[slot][0], reinterpret_cast<float*>(&s_acc[slot][0][0]), L);
-                if constexpr (MODE == kModeBand) {
-                    finish_piece(d);
-                } else if (L.lane == 0) {
+                if (L.lane == 0) {
                     // units of this stream's band: [SG pref[b] + band Tb, + Tb); with them,
                     // where the run's result goes
                     const int band = d.s / SPW;
@@ -1552,7 +1443,7 @@ pa_decode_balanced(DecodeArgs a) {
                 if constexpr (DEPTH == 1) load_tile(min(inext, nk - 1), dsc[nxt], kb[nxt], vb[nxt], qb);
                 else load_tile(min(inext, nk - 1), dsc[nxt], kb[nxt], vb[nxt], qr[nxt]);
                 __builtin_amdgcn_sched_barrier(0);
-                if (i + d == 0 && !bandwg) {
+                if (i + d == 0) {
                     clear_my_slots();
                     if (wave == NW - 1) write_records();
                 }
@@ -1566,13 +1457,11 @@ pa_decode_balanced(DecodeArgs a) {
         // outstanding into registers the compiler may reuse; otherwise it inserts waits
         // into every iteration.)
         if (PA_BAL_PRIO) set_wave_priority(0);
-    } else if constexpr (MODE != kModeBand) {
+    } else {
         // no tiles: empty slots, and the records from the last wave all the same
         clear_my_slots();
         if (wave == NW - 1) write_records();
     }
-    // One workgroup per band: every run was folded by its last wave; nothing is left.
-    if constexpr (MODE == kModeBand) return;
     __syncthreads();
 
     // Runs of slots: the non-empty slots of one stream are adjacent (waves of one stream
@@ -1604,7 +1493,7 @@ pa_decode_balanced(DecodeArgs a) {
         }
         return pos;
     };
-    if (g1 == g0 && !bandwg) {
+    if (g1 == g0) {
         // no units: empty triples (weight 0) for a merge whose band spans this
         // workgroup's (empty) range
         const size_t wslot = (size_t)w * 2 * SPW * HP;
@@ -1727,7 +1616,7 @@ pa_decode_balanced(DecodeArgs a) {
             for (int j = 0; j < EPT; ++j) {
                 if (complete) {
                     reinterpret_cast<float4_t*>(a.out + (row0 + h[j]) * D)[d4[j]] = o[j] / Ls[j];
-                } else if (!bandwg) {   // (a band held by one workgroup is always complete)
+                } else {
                     const size_t wrow = (((size_t)w * 2 + (tb == g0 ? 0 : 1)) * SPW + spr) * HP + h[j];
                     reinterpret_cast<float4_t*>(a.ws_acc + wrow * D)[d4[j]] = o[j];
                     if (d4[j] == 0) {
@@ -2070,15 +1959,13 @@ hipError_t launch_balanced_nw(const Plan& pl, const DecodeArgs& args, int ws_slo
         return use_row ? pa_decode_balanced<D, HP, kBalDepth, NW, SPLIT, kRow, M>
                        : pa_decode_balanced<D, HP, kBalDepth, NW, SPLIT, false, M>;
     };
-    const auto kern = pl.band_per_wg ? pick(IntC<kModeBand>())
-                      : args.single_launch ? pick(IntC<kModeSingle>())
-                                           : pick(IntC<kModeSplit>());
-    const int grid = pl.band_per_wg ? pl.prob.batch * pl.bands : balanced_grid();
+    const auto kern = args.single_launch ? pick(IntC<kModeSingle>()) : pick(IntC<kModeSplit>());
+    const int grid = balanced_grid();
     if (grid <= 0) return hipErrorInvalidDevice;
-    if (!pl.band_per_wg && grid > ws_slots) return hipErrorInvalidValue;   // the workspace holds fewer workgroups' rows
+    if (grid > ws_slots) return hipErrorInvalidValue;   // the workspace holds fewer workgroups' rows
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NW * 64), lds, stream, args);
     hipError_t err = hipGetLastError();
-    if (err != hipSuccess || args.single_launch || pl.band_per_wg) return err;
+    if (err != hipSuccess || args.single_launch) return err;
     hipLaunchKernelGGL((pa_merge_balanced<D, HP>), dim3((unsigned)grid), dim3(kMergeThreads), 0, stream, args);
     return hipGetLastError();
 }
@@ -2162,7 +2049,7 @@ hipError_t launch(const Plan& pl, const void* q, const void* k, const void* v,
     const pa_problem& p = pl.prob;
     // the single-launch merge folds at most kArrivalGroup groups of kArrivalGroup pieces, so
     // a band may span at most that many workgroups (checked before anything is enqueued)
-    if (pl.single_launch && pl.balanced && !pl.band_per_wg &&
+    if (pl.single_launch && pl.balanced &&
         device_compute_units() > kArrivalGroup * kArrivalGroup)
         return hipErrorInvalidConfiguration;
     float* ws_acc = nullptr;

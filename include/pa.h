@@ -112,7 +112,9 @@ typedef struct pa_problem {
     int32_t max_pages_per_sequence; /* row stride of block_tables                                 */
     int32_t num_physical_pages;     /* pages in each of key_cache / value_cache (pa_append writes
                                        only below it)                                             */
-    int32_t partition_size;         /* 0: the library splits the work (default).  > 0: no
+    int32_t partition_size;         /* 0: the library splits the work (default; when the bound
+                                       below keeps every context short, each sequence is one
+                                       partition and no workspace is needed).  > 0: no
                                        partial (max, sum, acc) triple covers more than this many
                                        tokens of a context; a multiple of page_size, at most 512
                                        pages.  The default split runs when the problem's sizes

@@ -115,7 +115,7 @@ def test_workspace_size():
     # the streams read side by side x heads_per_wg rows of (D + 2) floats, plus two 16-byte
     # records.  Streams side by side: gcd(streams, 12), halved while the batch holds fewer
     # than 32 bands.  Group 4 -> 4 heads per wave; 2 KV heads, batch 2 -> 2 bands -> 1.
-    # (A table of 64 pages: bands longer than the one-workgroup-per-band limit.)
+    # (A table of 64 pages: bands longer than the short-context limit.)
     L = dict(max_pages_per_sequence=64, num_physical_pages=256)
     assert ws_size(**L) == 1024 * 2 * 1 * 4 * (128 + 2) * 4 + 1024 * 32
     # 32 sequences: 32 bands of 2 streams, kept side by side
@@ -131,7 +131,7 @@ def test_workspace_size():
 
 def test_short_bands_need_no_workspace():
     # every band at most 24 stream tiles (table of 8 pages of 16: 8 tiles x 1 stream side by
-    # side): one workgroup per band, no merge, no workspace
+    # side): each sequence is one partition of the fixed route -- no merge, no workspace
     assert ws_size() == 0
     assert ws_size(max_pages_per_sequence=24, num_physical_pages=64) == 0     # 24 tiles x 1
     assert ws_size(max_pages_per_sequence=25, num_physical_pages=64) > 0      # 25 tiles
@@ -139,8 +139,10 @@ def test_short_bands_need_no_workspace():
     # 2 streams side by side (32 sequences): 12 tiles x 2 fits, 13 x 2 does not
     assert ws_size(batch=32, max_pages_per_sequence=12, num_physical_pages=512) == 0
     assert ws_size(batch=32, max_pages_per_sequence=13, num_physical_pages=512) > 0
-    # more bands than workgroups (2048 sequences x 2 bands): the even split
-    assert ws_size(batch=2048, num_physical_pages=20000) > 0
+    # any batch size (2048 sequences): still one partition per sequence
+    assert ws_size(batch=2048, num_physical_pages=20000) == 0
+    # a route flag or a partition size keeps the caller's choice
+    assert ws_size(flags=pa.PA_FLAG_FORCE_SPLIT) > 0
     # the debug bitmap still needs its words
     assert ws_size(flags=pa.PA_FLAG_DEBUG_BOUNDS) == 256
 
@@ -149,7 +151,7 @@ def test_workspace_size_with_partition_size():
     # a partition size may run either route (the balanced one when its partials fit it):
     # the larger of the two layouts.  Fixed partitions of one page -> 8 partitions of
     # (D + 2) floats per (sequence, head); the balanced layout with one stream side by side
-    # (a partition size never takes the one-workgroup-per-band shortcut).
+    # (a partition size never takes the one-partition-per-sequence shortcut).
     bal = 1024 * 2 * 1 * 4 * (128 + 2) * 4 + 1024 * 32
     assert ws_size(partition_size=16) == max(2 * 8 * 8 * (128 + 2) * 4, bal)
     assert ws_size(partition_size=16, max_context_length=40) == max(2 * 8 * 3 * (128 + 2) * 4, bal)

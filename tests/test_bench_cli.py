@@ -98,10 +98,13 @@ def test_committed_resources_cover_the_benched_kernels():
             group = spec["query_heads"] // spec["kv_heads"]
             page_size = spec["page_size"]
             head_dim = spec["head_dim"]
-        for band in (False, True):   # the even split, and one workgroup per band
-            names = bench.decode_kernel_names(_Wl, band)
+            batch = spec["batch"]
+            kv_heads = spec["kv_heads"]
+        # the even split, and short contexts (one partition per sequence, 8 or 4 waves)
+        for short, cus in ((False, 256), (True, 256), (True, 1)):
+            names = bench.decode_kernel_names(_Wl, short, cus)
             got = bench.kernel_resources(names)
-            assert got is not None and len(got) == len(names), (name, band)
+            assert got is not None and len(got) == len(names), (name, short, cus)
 
 
 def test_cpu_baseline_fields():

@@ -138,8 +138,8 @@ def test_shapes(shape, partition):
 
 
 SHORT = [
-    # (QH, KVH, D, ps, ctx): every band within the one-workgroup-per-band limit (at most 24
-    # stream tiles), so the call is one kernel and needs no workspace
+    # (QH, KVH, D, ps, ctx): every band within the short-context limit (at most 24 stream
+    # tiles), so each sequence is one partition: one kernel and no workspace
     (8, 2, 64, 16, [37, 100]),                  # the tiny workload's shape
     (32, 8, 128, 16, [1, 95, 60, 0, 17]),       # 2 streams side by side, an empty sequence
     (24, 4, 128, 8, [3, 64, 100]),              # pages of 8: tiles over two pages
@@ -149,13 +149,13 @@ SHORT = [
 
 
 @pytest.mark.parametrize("shape", SHORT, ids=lambda s: f"qh{s[0]}_kvh{s[1]}_d{s[2]}_ps{s[3]}")
-def test_short_bands_one_workgroup_each(shape):
+def test_short_contexts_one_partition_each(shape):
     QH, KVH, D, ps, ctx = shape
     wl = W.make_workload(name="short", batch=len(ctx), query_heads=QH, kv_heads=KVH, head_dim=D,
                          page_size=ps, context_lengths=ctx, pool="holes10", seed=7200 + QH + D + ps)
     dec = pa.decoder_for(wl, partition_size=0)
     try:
-        assert dec.workspace_bytes == 0, "expected the one-workgroup-per-band shortcut"
+        assert dec.workspace_bytes == 0, "expected one partition per sequence"
     finally:
         dec.close()
     C.decode_and_check(wl, partition_size=0, what=f"short bands {shape}")

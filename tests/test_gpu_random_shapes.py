@@ -113,7 +113,7 @@ def test_random_shape_debug_bounds(case):
 
 
 def _draw_short(seed):
-    """A shape whose bands are all short enough for one workgroup per band: heads per
+    """A shape whose bands are all short enough for one partition per sequence: heads per
     wave, streams and streams per band as the plan derives them, contexts up to the
     longest band that mode takes (24 stream tiles), with empty sequences and single
     tokens among them."""
@@ -141,14 +141,14 @@ def _draw_short(seed):
 
 @pytest.mark.parametrize("case", range(16))
 def test_random_short_bands(case):
-    """Seeded shapes that take one workgroup per band, where each stream's pieces are
-    folded by the last of its waves to finish one: up to 24 tiles per band, streams of 1
-    to 12 waves, waves with no tiles between others."""
+    """Seeded shapes with short contexts only, which take one partition per sequence (the
+    fixed kernel, 8 or 4 waves): up to 24 tiles per band, empty sequences and single
+    tokens, pages of 8 to 32."""
     d = _draw_short(9700 + case)
     wl = W.make_workload(name=f"short{case}", pool="holes10", seed=9750 + case, **d)
     dec = pa.decoder_for(wl, partition_size=0)
     try:
-        assert dec.workspace_bytes == 0, f"case {case}: expected one workgroup per band ({d})"
+        assert dec.workspace_bytes == 0, f"case {case}: expected one partition per sequence ({d})"
     finally:
         dec.close()
     C.decode_and_check(wl, partition_size=0,

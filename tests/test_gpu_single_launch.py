@@ -36,7 +36,7 @@ def _run_checked(wl, what, repeats=3):
         outs = []
         for _ in range(repeats):
             outs.append(dev.run(dec).clone())
-            if dec.workspace is None:   # short bands: one workgroup per band, no counters
+            if dec.workspace is None:   # short contexts: one partition per sequence, no counters
                 continue
             cnt = dec.workspace[-COUNTER_BYTES:].cpu().numpy().view(np.int32)
             assert not cnt.any(), f"{what}: arrival counters left non-zero: {np.flatnonzero(cnt)[:8]}"
