@@ -135,16 +135,23 @@ int build_plan(const pa_problem* in, Plan* pl) {
         out.rows_per_wg = (size_t)2 * out.spw * out.heads_per_wg;
         // units (band, 16-token tile) of the whole batch at most, from the host's bound
         out.balanced_units_max = (long long)out.bands * p.batch * ((p.max_context_length + 15LL) / 16);
-        // Short bands only (the host's bound): the even split would spread such a batch
-        // over all compute units, leave most of them idle and split every band over many
-        // workgroups.  Every sequence is then one partition of the fixed route instead: a
-        // workgroup per (sequence, KV head, head chunk) reads its own length, takes all the
-        // sequence's tiles and writes its rows -- no split to compute, no merge, no
-        // workspace (p2's single-tile fast path for every sequence).  Measured against one
-        // 12-wave workgroup per band on the balanced kernel (which this replaced): tiny
-        // 6.8 -> 5.0 us, and 30-39% less on seeded short shapes.
+        // Short contexts (the host's bound): every sequence is one partition of the fixed
+        // route -- a workgroup per (sequence, KV head, head chunk) reads its own length,
+        // takes all the sequence's tiles and writes its rows: no split to compute, no
+        // merge, no workspace (p2's single-tile fast path for every sequence).  Taken when
+        // the longest sequence needs at most kSingleMaxTilesPerWave tiles per wave of its
+        // workgroup and the grid has kSingleMinGrid workgroups, or when every band is short
+        // (the even split would then leave most compute units idle and split every band
+        // over many workgroups).  Measured against the even split, alternating in one
+        // process: 1.5-35% less on 11 shapes of 8 to 512 sequences up to 1024 tokens at up
+        // to 8 tiles per wave; 2-40% more at 16 or more tiles per wave (batch64 58.4 against
+        // 65.3 us) and on a 32-workgroup grid; tiny 6.8 -> 5.0 us.
         const long long band_tiles = (p.max_context_length + 15LL) / 16 * out.spw;
-        if (out.balanced && band_tiles <= kShortBandTiles) {
+        const long long grid_single = (long long)p.batch * p.kv_heads * out.n_chunks;
+        const long long waves_single = grid_single <= kPlanComputeUnits ? kFixedWavesWide : kFixedWaves;
+        const long long per_wave = ((p.max_context_length + 15LL) / 16 + waves_single - 1) / waves_single;
+        const bool single_fits = per_wave <= kSingleMaxTilesPerWave && grid_single >= kSingleMinGrid;
+        if (out.balanced && (band_tiles <= kShortBandTiles || single_fits)) {
             const long long t = ((long long)p.max_context_length + p.page_size - 1) / p.page_size * p.page_size;
             const int whole = (int)(t < p.page_size ? p.page_size : t);
             if (whole / p.page_size <= kMaxPartitionPages) {

@@ -32,10 +32,21 @@ constexpr size_t kNoallocCounterBytes = 64 * 1024;
 // Query heads one wave scores at once (MFMA rows are 16; LDS partial slots are sized
 // for this many heads).
 constexpr int kMaxHeadsPerWave = 8;
-// Short contexts: when no band of the balanced route could hold more than this many stream
-// tiles (about two per wave of a 12-wave workgroup; the host's bound), every sequence is
-// one partition of the fixed route instead.  Such a call needs no merge and no workspace.
+// Short contexts: every sequence is one partition of the fixed route (no merge, no
+// workspace) when the host's bound keeps the longest sequence within
+// kSingleMaxTilesPerWave tiles per wave of its workgroup and there are at least
+// kSingleMinGrid workgroups, or when no band of the balanced route could hold more than
+// kShortBandTiles stream tiles.
 constexpr int kShortBandTiles = 24;
+constexpr int kSingleMaxTilesPerWave = 8;
+constexpr int kSingleMinGrid = 64;
+// Waves per fixed-route workgroup: kFixedWavesWide when the grid is no larger than the
+// compute units, else kFixedWaves.
+constexpr int kFixedWaves = 4;
+constexpr int kFixedWavesWide = 8;
+// The plan is made at pa_create, which makes no HIP call: its route choice assumes the
+// compute units of an MI355X.  (Each call still sizes its grids from the device.)
+constexpr int kPlanComputeUnits = 256;
 
 struct Plan {
     pa_problem prob;        // validated copy, defaults resolved

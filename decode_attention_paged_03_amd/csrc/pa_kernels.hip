@@ -1913,7 +1913,7 @@ pa_bad_entries_kernel(const int32_t* bt, const int32_t* ctx, int max_pages, int 
 }
 
 #ifndef PA_WAVES
-#define PA_WAVES 4   // waves per decode workgroup (fixed route)
+#define PA_WAVES kFixedWaves   // waves per decode workgroup (fixed route)
 #endif
 #ifndef PA_DEPTH
 // tile buffers per wave (fixed route): one buffer leaves registers for more resident waves;
@@ -1925,7 +1925,7 @@ pa_bad_entries_kernel(const int32_t* bt, const int32_t* ctx, int max_pages, int 
 #define PA_BAL_DEPTH 1   // tile buffers per wave (balanced route)
 #endif
 constexpr int kWaves = PA_WAVES;
-constexpr int kWavesWide = 8;   // fixed route, at most one workgroup per compute unit
+constexpr int kWavesWide = kFixedWavesWide;   // fixed route, at most one workgroup per compute unit
 constexpr int kDepth = PA_DEPTH;
 constexpr int kBalDepth = PA_BAL_DEPTH;
 

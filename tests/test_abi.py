@@ -115,8 +115,8 @@ def test_workspace_size():
     # the streams read side by side x heads_per_wg rows of (D + 2) floats, plus two 16-byte
     # records.  Streams side by side: gcd(streams, 12), halved while the batch holds fewer
     # than 32 bands.  Group 4 -> 4 heads per wave; 2 KV heads, batch 2 -> 2 bands -> 1.
-    # (A table of 64 pages: bands longer than the short-context limit.)
-    L = dict(max_pages_per_sequence=64, num_physical_pages=256)
+    # (A table of 128 pages: sequences longer than the one-partition-per-sequence limit.)
+    L = dict(max_pages_per_sequence=128, num_physical_pages=512)
     assert ws_size(**L) == 1024 * 2 * 1 * 4 * (128 + 2) * 4 + 1024 * 32
     # 32 sequences: 32 bands of 2 streams, kept side by side
     assert ws_size(batch=32, **L) == 1024 * 2 * 2 * 4 * (128 + 2) * 4 + 1024 * 32
@@ -129,17 +129,24 @@ def test_workspace_size():
     assert ws_size(query_heads=24, kv_heads=4, batch=32, **L) == 1024 * 2 * 4 * 6 * (128 + 2) * 4 + 1024 * 32
 
 
-def test_short_bands_need_no_workspace():
-    # every band at most 24 stream tiles (table of 8 pages of 16: 8 tiles x 1 stream side by
-    # side): each sequence is one partition of the fixed route -- no merge, no workspace
-    assert ws_size() == 0
+def test_short_contexts_need_no_workspace():
+    # Each sequence is one partition of the fixed route -- no merge, no workspace -- when
+    # every band is short (at most 24 stream tiles), or when the longest sequence needs at
+    # most 8 tiles per wave (8 waves per workgroup up to 256 workgroups, else 4) over at
+    # least 64 workgroups (batch x KV heads x head chunks; here 2 KV heads, one chunk).
+    assert ws_size() == 0                                                        # 8 tiles x 1
     assert ws_size(max_pages_per_sequence=24, num_physical_pages=64) == 0     # 24 tiles x 1
-    assert ws_size(max_pages_per_sequence=25, num_physical_pages=64) > 0      # 25 tiles
+    assert ws_size(max_pages_per_sequence=25, num_physical_pages=64) > 0      # 25, 4 workgroups
     assert ws_size(max_context_length=384, max_pages_per_sequence=64, num_physical_pages=256) == 0
-    # 2 streams side by side (32 sequences): 12 tiles x 2 fits, 13 x 2 does not
-    assert ws_size(batch=32, max_pages_per_sequence=12, num_physical_pages=512) == 0
-    assert ws_size(batch=32, max_pages_per_sequence=13, num_physical_pages=512) > 0
-    # any batch size (2048 sequences): still one partition per sequence
+    # 32 sequences (64 workgroups of 8 waves): 64 tiles fit, 65 do not
+    assert ws_size(batch=32, max_pages_per_sequence=64, num_physical_pages=4096) == 0
+    assert ws_size(batch=32, max_pages_per_sequence=65, num_physical_pages=4096) > 0
+    # 256 sequences (512 workgroups of 4 waves): 32 tiles fit, 33 do not
+    assert ws_size(batch=256, max_pages_per_sequence=32, num_physical_pages=16384) == 0
+    assert ws_size(batch=256, max_pages_per_sequence=33, num_physical_pages=16384) > 0
+    # 16 sequences: 32 workgroups are too few for the per-wave rule
+    assert ws_size(batch=16, max_pages_per_sequence=32, num_physical_pages=1024) > 0
+    # any batch size of short sequences (2048): still one partition per sequence
     assert ws_size(batch=2048, num_physical_pages=20000) == 0
     # a route flag or a partition size keeps the caller's choice
     assert ws_size(flags=pa.PA_FLAG_FORCE_SPLIT) > 0
