@@ -618,7 +618,7 @@ def measure(W, pa, wl, args, stream, steps, warmup, append_steps=0, copy_calibra
         },
     }
     if balanced:
-        # the default route needs no workspace only with one workgroup per band
+        # the default route needs no workspace only when it takes one partition per sequence
         cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
         res["roofline"]["resources"] = kernel_resources(decode_kernel_names(wl, dec.workspace_bytes == 0, cus))
     if append_line:

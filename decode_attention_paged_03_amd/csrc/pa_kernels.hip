@@ -21,7 +21,10 @@
 //  * Fixed partitions (a partition size or a flag given): one workgroup per (sequence,
 //    KV head, head chunk, partition of partition_size tokens), partition triples in the
 //    workspace, pa_merge_kernel per (sequence, query head) -- the PARTITION_SIZE scheme of
-//    the "paged_attention_v2_pytorch.py" commit page.
+//    the "paged_attention_v2_pytorch.py" commit page.  When the host's bound keeps every
+//    context short, the plan takes this route with one partition per sequence: each
+//    workgroup writes its rows, with no merge and no workspace (that page's single-tile
+//    fast path for the whole batch).
 //
 // Both combine triples as M = max m_p, L = sum exp(m_p - M) l_p,
 // out = sum exp(m_p - M) acc_p / L (the V4 merge kernel's combination, with the global

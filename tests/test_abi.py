@@ -178,7 +178,7 @@ def test_workspace_size_single_launch():
     SL = pa.PA_FLAG_SINGLE_LAUNCH
     assert ws_size(flags=SL, **L) == ws_size(**L) + 1024 * 3 * 4
     assert ws_size(flags=SL | pa.PA_FLAG_DEBUG_BOUNDS, **L) == 256 + ws_size(**L) + 1024 * 3 * 4
-    # short bands are one kernel with no workspace anyway
+    # short contexts are one kernel with no workspace anyway (one partition per sequence)
     assert ws_size(flags=SL) == 0
 
 

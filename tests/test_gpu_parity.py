@@ -158,7 +158,7 @@ def test_short_contexts_one_partition_each(shape):
         assert dec.workspace_bytes == 0, "expected one partition per sequence"
     finally:
         dec.close()
-    C.decode_and_check(wl, partition_size=0, what=f"short bands {shape}")
+    C.decode_and_check(wl, partition_size=0, what=f"short contexts {shape}")
 
 
 @pytest.mark.parametrize("partition", [0, 256])

@@ -152,5 +152,5 @@ def test_random_short_bands(case):
     finally:
         dec.close()
     C.decode_and_check(wl, partition_size=0,
-                       what=f"short bands case {case}: QH{d['query_heads']}/KVH{d['kv_heads']} "
+                       what=f"short contexts case {case}: QH{d['query_heads']}/KVH{d['kv_heads']} "
                             f"D{d['head_dim']} ps{d['page_size']} B{d['batch']}")
