@@ -1,4 +1,6 @@
-"""Seeded random problem shapes through the default (balanced) route, against the oracle.
+"""Seeded random problem shapes against the oracle: through the library's own route (the
+balanced split, or one partition per sequence for short contexts), fixed partitions, the
+single launch and the bounds-checking flag.
 
 Each case draws a batch size, a head layout (KV heads and group size, hence heads per wave
 and streams per sequence), a head dimension, a page size and a mix of context lengths
@@ -140,7 +142,7 @@ def _draw_short(seed):
 
 
 @pytest.mark.parametrize("case", range(16))
-def test_random_short_bands(case):
+def test_random_short_contexts(case):
     """Seeded shapes with short contexts only, which take one partition per sequence (the
     fixed kernel, 8 or 4 waves): up to 24 tiles per band, empty sequences and single
     tokens, pages of 8 to 32."""
@@ -153,4 +155,49 @@ def test_random_short_bands(case):
         dec.close()
     C.decode_and_check(wl, partition_size=0,
                        what=f"short contexts case {case}: QH{d['query_heads']}/KVH{d['kv_heads']} "
+                            f"D{d['head_dim']} ps{d['page_size']} B{d['batch']}")
+
+
+def _draw_wide_short(seed):
+    """A shape for the other short-context rule: at least 64 workgroups (sequences x KV
+    heads x head chunks) and the longest sequence within 8 tiles per wave (1024 tokens
+    with 8 waves when the grid fits 256 compute units, 512 with 4), with empty sequences
+    and single tokens among them."""
+    import math
+    rng = np.random.default_rng(seed)
+    kv_heads = int(rng.choice([2, 4, 8]))
+    group = int(rng.choice([1, 2, 4, 6, 8, 16]))
+    hp = max(h for h in range(1, 9) if group % h == 0)
+    per_seq = kv_heads * (group // hp)
+    lo = math.ceil(64 / per_seq)
+    batch = int(rng.integers(lo, max(lo + 1, 600 // per_seq + 1)))
+    waves = 8 if batch * per_seq <= 256 else 4
+    page_size = int(rng.choice([8, 16, 32]))
+    longest = 16 * 8 * waves // page_size * page_size
+    ctx = rng.integers(0, longest + 1, size=batch)
+    ctx[rng.random(batch) < 0.1] = 0
+    ctx[rng.random(batch) < 0.1] = 1
+    # keep the oracle's work bounded (about 40 M token-heads per case)
+    if int(ctx.sum()) * kv_heads * group > 40_000_000:
+        ctx = (ctx * (40_000_000 / (int(ctx.sum()) * kv_heads * group))).astype(np.int64)
+    ctx[int(rng.integers(0, batch))] = longest
+    return dict(batch=batch, query_heads=kv_heads * group, kv_heads=kv_heads,
+                head_dim=int(rng.choice([64, 128])), page_size=page_size,
+                context_lengths=[int(c) for c in ctx])
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_random_wide_short_contexts(case):
+    """Seeded shapes of many short sequences (at least 64 workgroups, at most 8 tiles per
+    wave), which also take one partition per sequence, on grids both within and beyond
+    the compute units (8 and 4 waves per workgroup)."""
+    d = _draw_wide_short(9800 + case)
+    wl = W.make_workload(name=f"wide_short{case}", pool="holes10", seed=9850 + case, **d)
+    dec = pa.decoder_for(wl, partition_size=0)
+    try:
+        assert dec.workspace_bytes == 0, f"case {case}: expected one partition per sequence ({d})"
+    finally:
+        dec.close()
+    C.decode_and_check(wl, partition_size=0,
+                       what=f"wide short contexts case {case}: QH{d['query_heads']}/KVH{d['kv_heads']} "
                             f"D{d['head_dim']} ps{d['page_size']} B{d['batch']}")
